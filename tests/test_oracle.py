@@ -1,0 +1,353 @@
+"""Pins for the float64 oracle (CPU only).
+
+The oracle is checked against things other than itself: a pure-Python brute
+force, closed forms (identical keys / zero query give the mean of V; one
+token gives V[0] exactly), torch's float64 SDPA with ``enable_gqa`` (a library
+routine whose GQA mapping is the contiguous one), invariants (page
+permutation, repeat_kv expansion, split count, key shift, convex hull) and
+the KV-size ratio printed on the GQA/TensorRT page. A few tests plant a
+mistake in the oracle and check that a pin catches it.
+"""
+
+import json
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import attention as oa
+from oracle import brute
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tol_close(a, b, rel=1e-13):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = max(1.0, float(np.abs(b).max()) if b.size else 1.0)
+    return float(np.abs(a - b).max()) <= rel * scale if a.size else True
+
+
+def _small_decode(seed, B, hq, hkv, D, P, lens, dtype="f32", **kw):
+    return synth.decode_inputs(B, hq, hkv, D, P, lens, dtype, seed=seed, pad_pages=3, **kw)
+
+
+def _contiguous_to_paged(kc, vc, P, seed, pad=2):
+    """Test-side scatter of contiguous K/V [B][Hkv][T][D] into a permuted pool."""
+    B, hkv, T, D = kc.shape
+    npg = (T + P - 1) // P
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(B * npg + pad, generator=g)[: B * npg]
+    pool_k = torch.full((B * npg + pad, hkv, P, D), float("nan"), dtype=kc.dtype)
+    pool_v = pool_k.clone()
+    pt = torch.full((B, npg + 1), -1, dtype=torch.int32)
+    for b in range(B):
+        for i in range(npg):
+            phys = int(perm[b * npg + i])
+            pt[b, i] = phys
+            for s in range(P):
+                t = i * P + s
+                if t < T:
+                    pool_k[phys, :, s, :] = kc[b, :, t, :]
+                    pool_v[phys, :, s, :] = vc[b, :, t, :]
+    return pool_k, pool_v, pt
+
+
+# ---------------------------------------------------------------- brute force
+
+DECODE_CASES = [
+    # B, Hq, Hkv, D, P, lens
+    (1, 1, 1, 1, 1, [5]),
+    (2, 2, 1, 3, 4, [7, 1]),
+    (2, 4, 2, 8, 4, [23, 16]),
+    (1, 8, 2, 5, 8, [17]),
+    (2, 4, 4, 4, 8, [9, 0]),
+    (2, 8, 1, 6, 1, [3, 11]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_decode_matches_brute_force(case):
+    B, hq, hkv, D, P, lens = case
+    x = _small_decode(11 + len(lens) + D, B, hq, hkv, D, P, lens)
+    got = oracle.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, x.scale)
+    ref = brute.decode(x.q.double().tolist(), x.k_cache.double().tolist(),
+                       x.v_cache.double().tolist(), x.page_table.tolist(),
+                       x.context_lens.tolist(), x.scale)
+    assert _tol_close(got, ref)
+    assert np.isfinite(got).all()
+
+
+PREFILL_CASES = [(1, 1, 1, 1, 2), (2, 5, 2, 1, 3), (1, 9, 4, 2, 8), (2, 6, 8, 2, 4), (1, 7, 4, 4, 5)]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES)
+def test_prefill_matches_brute_force(case):
+    B, S, hq, hkv, D = case
+    x = synth.prefill_inputs(B, S, hq, hkv, D, 4, seed=21 + S, dtype="f32")
+    got = oracle.prefill_causal(x.q, x.k, x.v, x.scale)
+    ref = brute.prefill(x.q.double().tolist(), x.k.double().tolist(), x.v.double().tolist(), x.scale)
+    assert _tol_close(got, ref)
+
+
+# ------------------------------------------------------------- closed forms
+
+def test_identical_keys_give_mean_of_values():
+    x = _small_decode(5, 2, 8, 2, 16, 4, [13, 30])
+    k0 = torch.randn(16, generator=torch.Generator().manual_seed(3))
+    kc = x.k_cache.clone()
+    kc[:] = k0  # every key row identical (pads too; they are never read)
+    got = oracle.decode_paged(x.q, kc, x.v_cache, x.page_table, x.context_lens, x.scale)
+    for b in range(2):
+        T = int(x.context_lens[b])
+        for h in range(8):
+            g = h // 4
+            vals = [x.v_cache[int(x.page_table[b, t // 4]), g, t % 4].double() for t in range(T)]
+            mean = torch.stack(vals).mean(0).numpy()
+            assert np.abs(got[b, h] - mean).max() <= 1e-13
+
+
+def test_zero_query_gives_mean_of_values():
+    x = _small_decode(6, 1, 4, 1, 8, 8, [21])
+    q0 = torch.zeros_like(x.q)
+    got = oracle.decode_paged(q0, x.k_cache, x.v_cache, x.page_table, x.context_lens, x.scale)
+    vals = [x.v_cache[int(x.page_table[0, t // 8]), 0, t % 8].double() for t in range(21)]
+    mean = torch.stack(vals).mean(0).numpy()
+    assert np.abs(got[0] - mean[None, :]).max() <= 1e-13
+
+
+def test_single_token_is_exact_value_row():
+    x = _small_decode(7, 2, 4, 2, 8, 4, [1, 1])
+    got = oracle.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, x.scale)
+    for b in range(2):
+        for h in range(4):
+            v0 = x.v_cache[int(x.page_table[b, 0]), h // 2, 0].double().numpy()
+            assert np.array_equal(got[b, h], v0)
+
+
+def test_prefill_identical_keys_give_running_mean():
+    x = synth.prefill_inputs(1, 12, 4, 2, 8, 4, seed=9, dtype="f32")
+    k = x.k.clone()
+    k[:] = 0.5
+    got = oracle.prefill_causal(x.q, k, x.v, x.scale)
+    v = x.v.double().numpy()
+    for i in range(12):
+        for h in range(4):
+            mean = v[0, : i + 1, h // 2, :].mean(0)
+            assert np.abs(got[0, i, h] - mean).max() <= 1e-13
+    # row 0 sees only key 0: exactly V[0]
+    for h in range(4):
+        assert np.array_equal(got[0, 0, h], v[0, 0, h // 2])
+
+
+# ------------------------------------------------------ library routine (SDPA)
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 8), (4, 1), (32, 8)])
+def test_decode_matches_torch_sdpa_gqa(hq, hkv):
+    B, T, D, P = 2, 37, 16, 8
+    g = torch.Generator().manual_seed(hq * 100 + hkv)
+    q = torch.randn(B, hq, D, generator=g, dtype=torch.float64)
+    kc = torch.randn(B, hkv, T, D, generator=g, dtype=torch.float64)
+    vc = torch.randn(B, hkv, T, D, generator=g, dtype=torch.float64)
+    pk, pv, pt = _contiguous_to_paged(kc, vc, P, seed=hq + hkv)
+    lens = torch.full((B,), T, dtype=torch.int32)
+    scale = 1 / math.sqrt(D)
+    got = oracle.decode_paged(q, pk, pv, pt, lens, scale)
+    ref = F.scaled_dot_product_attention(q[:, :, None, :], kc, vc, scale=scale,
+                                         enable_gqa=True)[:, :, 0, :]
+    assert np.abs(got - ref.numpy()).max() <= 1e-12
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (8, 1)])
+def test_prefill_matches_torch_sdpa_causal_gqa(hq, hkv):
+    B, S, D = 2, 29, 8
+    g = torch.Generator().manual_seed(7 * hq + hkv)
+    q = torch.randn(B, S, hq, D, generator=g, dtype=torch.float64)
+    k = torch.randn(B, S, hkv, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, S, hkv, D, generator=g, dtype=torch.float64)
+    scale = 1 / math.sqrt(D)
+    got = oracle.prefill_causal(q, k, v, scale)
+    ref = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2).contiguous(),
+                                         v.transpose(1, 2).contiguous(), scale=scale,
+                                         is_causal=True, enable_gqa=True).transpose(1, 2)
+    assert np.abs(got - ref.numpy()).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_repeat_kv_expansion_is_identical_mha():
+    x = _small_decode(8, 2, 8, 2, 8, 4, [19, 6])
+    gqa = oracle.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, x.scale)
+    ke = x.k_cache.repeat_interleave(4, dim=1)
+    ve = x.v_cache.repeat_interleave(4, dim=1)
+    mha = oracle.decode_paged(x.q, ke, ve, x.page_table, x.context_lens, x.scale)
+    assert np.array_equal(gqa, mha)
+
+
+def test_page_permutation_leaves_output_bit_identical():
+    x = _small_decode(9, 3, 8, 2, 8, 4, [17, 4, 30])
+    base = oracle.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, x.scale)
+    n = x.k_cache.shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(1))  # old -> new id
+    k2 = torch.empty_like(x.k_cache)
+    v2 = torch.empty_like(x.v_cache)
+    k2[perm] = x.k_cache
+    v2[perm] = x.v_cache
+    pt2 = x.page_table.clone()
+    live = pt2 >= 0
+    pt2[live] = perm[pt2[live].long()].to(torch.int32)
+    moved = oracle.decode_paged(x.q, k2, v2, pt2, x.context_lens, x.scale)
+    assert np.array_equal(base, moved)
+
+
+@pytest.mark.parametrize("ns", [1, 2, 3, 4, 8, 16])
+def test_split_and_combine_equals_unsplit(ns):
+    x = _small_decode(10, 3, 4, 2, 8, 4, [45, 7, 64])
+    ref = oracle.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, x.scale)
+    o, lse = oracle.decode_split_partials(x.q, x.k_cache, x.v_cache, x.page_table,
+                                          x.context_lens, x.scale, ns)
+    assert _tol_close(oracle.combine_splits(o, lse), ref)
+    # an empty split is marked -inf with a zero output
+    for b, T in enumerate([45, 7, 64]):
+        npg = -(-T // 4)
+        for s, (lo, hi) in enumerate(oracle.split_page_ranges(npg, ns)):
+            if hi <= lo:
+                assert np.all(lse[b, :, s] == -np.inf) and np.all(o[b, :, s] == 0)
+
+
+def test_split_lse_matches_brute_logsumexp():
+    x = _small_decode(12, 1, 2, 1, 4, 4, [10])
+    o, lse = oracle.decode_split_partials(x.q, x.k_cache, x.v_cache, x.page_table,
+                                          x.context_lens, x.scale, 3)
+    q = x.q.double().tolist()
+    for s, (lo, hi) in enumerate(oracle.split_page_ranges(3, 3)):
+        for h in range(2):
+            scores = []
+            for t in range(lo * 4, min(hi * 4, 10)):
+                p = int(x.page_table[0, t // 4])
+                k = x.k_cache[p, 0, t % 4].double().tolist()
+                scores.append(x.scale * math.fsum(q[0][h][c] * k[c] for c in range(4)))
+            m = max(scores)
+            expect = m + math.log(math.fsum(math.exp(v - m) for v in scores))
+            assert abs(lse[0, h, s] - expect) <= 1e-13 * max(1.0, abs(expect))
+
+
+def test_split_page_ranges_cover_exactly():
+    for n in range(0, 40):
+        for ns in (1, 2, 3, 4, 8, 16):
+            r = oracle.split_page_ranges(n, ns)
+            assert len(r) == ns
+            covered = [p for lo, hi in r for p in range(lo, hi)]
+            assert covered == list(range(n))
+
+
+def test_combine_special_cases():
+    rng = np.random.default_rng(0)
+    o = rng.standard_normal((4, 5, 3))
+    lse = np.full((4, 5), -np.inf)
+    out = oracle.combine_splits(o, lse)
+    assert np.all(out == 0)  # all splits empty -> zero
+    lse[1, 2] = 0.3  # one live split -> that split's output exactly
+    out = oracle.combine_splits(o, lse)
+    assert np.array_equal(out[1], o[1, 2])
+    lse[2, :] = 1.25  # equal weights -> plain mean
+    out = oracle.combine_splits(o, lse)
+    assert np.abs(out[2] - o[2].mean(0)).max() <= 1e-15
+    lse[3] = rng.standard_normal(5)  # a common shift of all lse changes nothing
+    a = oracle.combine_splits(o[3:4], lse[3:4])
+    b = oracle.combine_splits(o[3:4], lse[3:4] + 40.0)
+    assert np.abs(a - b).max() <= 1e-14
+
+
+def test_convex_hull_and_key_shift():
+    x = _small_decode(13, 2, 4, 2, 8, 4, [33, 12])
+    out = oracle.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, x.scale)
+    shifted = x.k_cache.double()  # shift in float64 so the inputs stay exact
+    u = torch.randn(8, generator=torch.Generator().manual_seed(4), dtype=torch.float64)
+    shifted += u  # every key of every head moves by the same vector
+    out2 = oracle.decode_paged(x.q, shifted, x.v_cache, x.page_table, x.context_lens, x.scale)
+    assert np.abs(out - out2).max() <= 1e-12
+    for b, T in enumerate([33, 12]):
+        for h in range(4):
+            vals = np.stack([x.v_cache[int(x.page_table[b, t // 4]), h // 2, t % 4].double().numpy()
+                             for t in range(T)])
+            assert np.all(out[b, h] >= vals.min(0) - 1e-14)
+            assert np.all(out[b, h] <= vals.max(0) + 1e-14)
+
+
+def test_gather_identity_and_permuted():
+    kc = torch.randn(2, 3, 21, 4, dtype=torch.float64)
+    vc = torch.randn(2, 3, 21, 4, dtype=torch.float64)
+    pk, pv, pt = _contiguous_to_paged(kc, vc, 8, seed=3)
+    lens = torch.tensor([21, 9], dtype=torch.int32)
+    got = oracle.gather_paged(pk, pt, lens, 8)
+    assert torch.equal(got[0], kc[0].transpose(0, 1))
+    assert torch.equal(got[1], kc[1, :, :9].transpose(0, 1))
+
+
+def test_append_round_trip_and_untouched_pages():
+    x = synth.prefill_inputs(2, 37, 4, 2, 8, 8, seed=4, dtype="bf16")
+    kc = oracle.append_paged(x.k_cache, x.k, x.page_table, 8)
+    back = oracle.gather_paged(kc, x.page_table, torch.tensor([37, 37]), 8)
+    for b in range(2):
+        assert torch.equal(back[b], x.k[b])
+    used = set(int(p) for p in x.page_table.flatten())
+    for p in range(kc.shape[0]):
+        if p not in used:
+            assert torch.isnan(kc[p].float()).all()
+
+
+def test_kv_size_ratio_golden():
+    with open(os.path.join(GOLDEN, "kv_cache_ratio.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        mha = oracle.kv_bytes(case["tokens"], case["query_heads"], 128, 2)
+        gqa = oracle.kv_bytes(case["tokens"], case["kv_heads"], 128, 2)
+        assert gqa / mha == pytest.approx(1 - case["reduction"], abs=0)
+
+
+# ------------------------------------------------ planted mistakes are caught
+
+def _sdpa_decode_error():
+    B, T, D, P, hq, hkv = 1, 20, 8, 4, 8, 2
+    g = torch.Generator().manual_seed(99)
+    q = torch.randn(B, hq, D, generator=g, dtype=torch.float64)
+    kc = torch.randn(B, hkv, T, D, generator=g, dtype=torch.float64)
+    vc = torch.randn(B, hkv, T, D, generator=g, dtype=torch.float64)
+    pk, pv, pt = _contiguous_to_paged(kc, vc, P, seed=5)
+    got = oa.decode_paged(q, pk, pv, pt, torch.tensor([T]), 1 / math.sqrt(D))
+    ref = F.scaled_dot_product_attention(q[:, :, None, :], kc, vc, enable_gqa=True)[:, :, 0, :]
+    return np.abs(got - ref.numpy()).max()
+
+
+def test_planted_interleaved_head_mapping_is_caught(monkeypatch):
+    assert _sdpa_decode_error() <= 1e-12
+    monkeypatch.setattr(oa, "kv_head_of", lambda h, hq, hkv: h % hkv)
+    assert _sdpa_decode_error() > 1e-3
+
+
+def test_planted_slot_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(oa, "logical_to_physical",
+                        lambda row, t, P: (int(row[t // P]), (t + 1) % P))
+    x = _small_decode(14, 1, 2, 1, 4, 4, [9])
+    x.k_cache[:] = x.k_cache.nan_to_num(0.0)
+    x.v_cache[:] = x.v_cache.nan_to_num(0.0)
+    got = oa.gather_paged(x.k_cache, x.page_table, x.context_lens, 4)[0]
+    want = torch.stack([x.k_cache[int(x.page_table[0, t // 4]), :, t % 4] for t in range(9)])
+    assert not torch.equal(got, want)
+
+
+def test_planted_off_by_one_causal_is_caught(monkeypatch):
+    x = synth.prefill_inputs(1, 6, 2, 1, 4, 4, seed=2, dtype="f32")
+    ref = brute.prefill(x.q.double().tolist(), x.k.double().tolist(), x.v.double().tolist(), x.scale)
+    real_triu = np.triu
+    monkeypatch.setattr(oa.np, "triu", lambda m, k=0: real_triu(m, k=k + 1))  # lets j == i+1 in
+    got = oa.prefill_causal(x.q, x.k, x.v, x.scale)
+    monkeypatch.undo()
+    assert not _tol_close(got, ref)
