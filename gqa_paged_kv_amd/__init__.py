@@ -1,0 +1,196 @@
+"""Python binding of libgqa (paged GQA attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gqa.h``. PyTorch provides the
+device memory (outputs and split workspace are allocated with torch) and the
+current stream. There is no fallback: if ``libgqa.so`` is missing or a call
+fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgqa.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
+F32, BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16}
+
+# Exported symbols and their C signatures (argument types in order).
+_p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "gqa_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _p, _p] + [_i] * 8 + [_f, _i, _p]),
+    "gqa_prefill_causal": (_i, [_p] * 7 + [_i] * 8 + [_f, _i, _p]),
+    "gqa_combine_splits": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "gqa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "gqa_status_string": (ctypes.c_char_p, [_i]),
+    "gqa_validate_decode": (_i, [_p] * 8 + [_i] * 8 + [_f, _i]),
+    "gqa_validate_prefill": (_i, [_p] * 7 + [_i] * 8 + [_f, _i]),
+    "gqa_validate_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _i]),
+    "gqa_gather_paged": (_i, [_p, _p, _p, _p] + [_i] * 7 + [_p]),
+}
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgqa.so (built by ``gqa_paged_kv_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gqa_paged_kv_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (ret, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = ret
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gqa_status_string(status).decode()
+
+
+def workspace_bytes(B: int, Hq: int, D: int, num_splits: int) -> int:
+    return int(load().gqa_decode_workspace_bytes(B, Hq, D, num_splits))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(st: int, what: str):
+    if st != OK:
+        raise GQAError(st, what)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions")
+
+
+def alloc_workspace(B: int, Hq: int, D: int, num_splits: int, device):
+    """fp32 split workspace (ws_o [B][Hq][NS][D], ws_lse [B][Hq][NS])."""
+    ws_o = torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=device)
+    ws_lse = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=device)
+    return ws_o, ws_lse
+
+
+def decode_paged(q, k_cache, v_cache, page_table, context_lens, num_splits: int = 1,
+                 scale: float | None = None, out=None, workspace=None):
+    """Paged GQA decode; returns out [B][Hq][D] in q's dtype (enqueued on the current stream)."""
+    lib = load()
+    _need(q, "q", dim=3)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    if page_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("page_table / context_lens batch mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype, 3)
+    ws_o = ws_lse = None
+    if num_splits > 1:
+        if workspace is None:
+            workspace = alloc_workspace(B, Hq, D, num_splits, q.device)
+        ws_o, ws_lse = workspace
+        _need(ws_o, "ws_o", torch.float32)
+        _need(ws_lse, "ws_lse", torch.float32)
+        if ws_o.numel() < B * Hq * num_splits * D or ws_lse.numel() < B * Hq * num_splits:
+            raise ValueError("workspace too small")
+    st = lib.gqa_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                              _ptr(context_lens), _ptr(out), _ptr(ws_o), _ptr(ws_lse), B, Hq, Hkv,
+                              D, P, page_table.shape[1], num_pages, num_splits, scale,
+                              _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st, "gqa_decode_paged")
+    return out
+
+
+def combine_splits(ws_o, ws_lse, out_dtype=torch.bfloat16, out=None):
+    """LSE merge of split partials; returns out [B][Hq][D]."""
+    lib = load()
+    _need(ws_o, "ws_o", torch.float32, 4)
+    _need(ws_lse, "ws_lse", torch.float32, 3)
+    B, Hq, ns, D = ws_o.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=ws_o.device)
+    st = lib.gqa_combine_splits(_ptr(ws_o), _ptr(ws_lse), _ptr(out), B, Hq, D, ns,
+                                _DTYPE_CODE[out.dtype], _stream(ws_o.device))
+    _check(st, "gqa_combine_splits")
+    return out
+
+
+def prefill_causal(q, k, v, k_cache, v_cache, page_table, scale: float | None = None, out=None):
+    """Causal GQA prefill; appends k/v into the paged cache; returns out [B][S][Hq][D]."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    num_pages, Hkv_c, P, Dc = k_cache.shape
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or Hkv_c != Hkv or Dc != D:
+        raise ValueError("prefill shapes do not match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.gqa_prefill_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(page_table), _ptr(out), B, S, Hq, Hkv, D, P,
+                                page_table.shape[1], num_pages, scale, BF16, _stream(q.device))
+    _check(st, "gqa_prefill_causal")
+    return out
+
+
+def gather_paged(cache, page_table, context_lens, dst=None):
+    """Test helper: contiguous copy [B][max_pages*P][Hkv][D] of the live tokens."""
+    lib = load()
+    _need(cache, "cache", None, 4)
+    num_pages, Hkv, P, D = cache.shape
+    B, max_pages = page_table.shape
+    if dst is None:
+        dst = torch.zeros((B, max_pages * P, Hkv, D), dtype=cache.dtype, device=cache.device)
+    st = lib.gqa_gather_paged(_ptr(cache), _ptr(page_table), _ptr(context_lens), _ptr(dst), B,
+                              Hkv, D, P, max_pages, num_pages, _DTYPE_CODE[cache.dtype],
+                              _stream(cache.device))
+    _check(st, "gqa_gather_paged")
+    return dst

@@ -1,0 +1,75 @@
+// extern "C" entry points of libgqa: validate on the host, then enqueue kernels on
+// the caller's stream. No allocation, no synchronisation, no global state.
+#include <hip/hip_runtime.h>
+
+#include "../../include/gqa.h"
+
+namespace gqa {
+struct bf16_t;
+int launch_decode_paged(const void* q, const void* k, const void* v, const int32_t* pt,
+                        const int32_t* lens, void* out, float* ws_o, float* ws_lse, int B,
+                        int Hq, int Hkv, int D, int max_pages, int ns, float scale, int dtype,
+                        hipStream_t s);
+int launch_combine(const float* ws_o, const float* ws_lse, void* out, int B, int Hq, int D,
+                   int ns, int dtype, hipStream_t s);
+int launch_gather(const void* cache, const int32_t* pt, const int32_t* lens, void* dst, int B,
+                  int Hkv, int D, int P, int max_pages, int dtype, hipStream_t s);
+int launch_append(const void* src, const int32_t* pt, void* cache, int B, int S, int Hkv, int D,
+                  int P, int max_pages, int elem_bytes, hipStream_t s);
+int launch_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
+                   int Hkv, int D, float scale, hipStream_t s);
+}  // namespace gqa
+
+extern "C" {
+
+int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* page_table, const int32_t* context_lens, void* out,
+                     float* ws_o, float* ws_lse, int B, int Hq, int Hkv, int D, int P,
+                     int max_pages, int num_pages, int num_splits, float scale, int dtype,
+                     void* stream) {
+  int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
+                               B, Hq, Hkv, D, P, max_pages, num_pages, num_splits, scale, dtype);
+  if (st != GQA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
+                                B, Hq, Hkv, D, max_pages, num_splits, scale, dtype, s);
+  if (st != GQA_OK || num_splits == 1) return st;
+  return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, num_splits, dtype, s);
+}
+
+int gqa_combine_splits(const float* ws_o, const float* ws_lse, void* out, int B, int Hq, int D,
+                       int num_splits, int out_dtype, void* stream) {
+  int st = gqa_validate_combine(ws_o, ws_lse, out, B, Hq, D, num_splits, out_dtype);
+  if (st != GQA_OK) return st;
+  return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, num_splits, out_dtype,
+                             (hipStream_t)stream);
+}
+
+int gqa_prefill_causal(const void* q, const void* k, const void* v, void* k_cache,
+                       void* v_cache, const int32_t* page_table, void* out, int B, int S,
+                       int Hq, int Hkv, int D, int P, int max_pages, int num_pages,
+                       float scale, int dtype, void* stream) {
+  int st = gqa_validate_prefill(q, k, v, k_cache, v_cache, page_table, out, B, S, Hq, Hkv, D, P,
+                                max_pages, num_pages, scale, dtype);
+  if (st != GQA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = gqa::launch_append(k, page_table, k_cache, B, S, Hkv, D, P, max_pages, 2, s);
+  if (st != GQA_OK) return st;
+  st = gqa::launch_append(v, page_table, v_cache, B, S, Hkv, D, P, max_pages, 2, s);
+  if (st != GQA_OK) return st;
+  return gqa::launch_prefill(q, k, v, out, B, S, Hq, Hkv, D, scale, s);
+}
+
+int gqa_gather_paged(const void* cache, const int32_t* page_table, const int32_t* context_lens,
+                     void* dst, int B, int Hkv, int D, int P, int max_pages, int num_pages,
+                     int dtype, void* stream) {
+  if (!cache || !page_table || !context_lens || !dst) return GQA_ERR_INVALID_ARG;
+  if (B <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_pages <= 0 || num_pages <= 0)
+    return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  if ((D != 64 && D != 128) || P != 16 || B > 65535) return GQA_ERR_UNSUPPORTED;
+  return gqa::launch_gather(cache, page_table, context_lens, dst, B, Hkv, D, P, max_pages, dtype,
+                            (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Host-side argument validation for the libgqa C ABI. Pure C++ (no HIP
+// headers): every rule here runs before anything is enqueued, so it is
+// testable on a machine without a GPU.
+//
+// Rules follow the statement of the problem on the pages: Hq query heads in
+// Hkv equal groups (page "TensorRT对Grouped Query Attention的支持进展",
+// section "技术演进背景"; non-uniform grouping is rejected), fixed-size
+// pages addressed through a page table (same page, section
+// "动态形状与KV Cache管理"), NumSplits >= 1 (page
+// "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
+// "核心参数调优：PackGQA与NumSplits的协同舞蹈").
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/gqa.h"
+
+namespace {
+
+constexpr int kMaxSplits = 256;
+constexpr int kMaxGridY = 65535;
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool supported_decode_group(int g) {
+  return g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32;
+}
+bool supported_prefill_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Shape checks common to decode and prefill.
+int check_common(int B, int Hq, int Hkv, int D, int P, int max_pages, int num_pages,
+                 float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_pages <= 0 || num_pages <= 0)
+    return GQA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if ((int64_t)B * max_pages > INT32_MAX) return GQA_ERR_INVALID_ARG;
+  if (!supported_head_dim(D) || P != 16) return GQA_ERR_UNSUPPORTED;
+  if (B > kMaxGridY) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GQA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t gqa_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * Hq * num_splits;
+  return rows * (size_t)D * sizeof(float) + rows * sizeof(float);
+}
+
+int gqa_validate_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, const int32_t* context_lens, const void* out,
+                        const float* ws_o, const float* ws_lse, int B, int Hq, int Hkv, int D,
+                        int P, int max_pages, int num_pages, int num_splits, float scale,
+                        int dtype) {
+  if (!q || !k_cache || !v_cache || !page_table || !context_lens || !out)
+    return GQA_ERR_INVALID_ARG;
+  if (num_splits < 1) return GQA_ERR_INVALID_ARG;
+  if (num_splits > 1 && (!ws_o || !ws_lse)) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  int st = check_common(B, Hq, Hkv, D, P, max_pages, num_pages, scale);
+  if (st != GQA_OK) return st;
+  if (!supported_decode_group(Hq / Hkv)) return GQA_ERR_UNSUPPORTED;
+  if (num_splits > kMaxSplits) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)Hkv * num_splits > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+int gqa_validate_prefill(const void* q, const void* k, const void* v, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const void* out, int B,
+                         int S, int Hq, int Hkv, int D, int P, int max_pages, int num_pages,
+                         float scale, int dtype) {
+  if (!q || !k || !v || !k_cache || !v_cache || !page_table || !out) return GQA_ERR_INVALID_ARG;
+  if (S <= 0) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  int st = check_common(B, Hq, Hkv, D, P, max_pages, num_pages, scale);
+  if (st != GQA_OK) return st;
+  if ((int64_t)max_pages * P < S) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (D != 128) return GQA_ERR_UNSUPPORTED;
+  if (!supported_prefill_group(Hq / Hkv)) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)S * Hq > INT32_MAX / 256) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+int gqa_validate_combine(const float* ws_o, const float* ws_lse, const void* out, int B, int Hq,
+                         int D, int num_splits, int out_dtype) {
+  if (!ws_o || !ws_lse || !out) return GQA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || D <= 0 || num_splits < 1) return GQA_ERR_INVALID_ARG;
+  if (out_dtype != GQA_F32 && out_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  if (!supported_head_dim(D)) return GQA_ERR_UNSUPPORTED;
+  if (num_splits > kMaxSplits) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+/*
+ * gqa.h -- C ABI of libgqa: fused grouped-query attention over a paged KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (page "TensorRT-LLM与TensorRT核心差异解析", chapter 4,
+ * section 4.1 and section 4.2.1): for every query row, out = softmax(scale *
+ * q K^T) V evaluated tile by tile on chip, so no score matrix ever reaches
+ * memory and only the output is written. Grouping (page "TensorRT对Grouped
+ * Query Attention的支持进展", section "技术演进背景"): Hq query heads are
+ * split into Hkv contiguous groups of G = Hq / Hkv heads; query head h reads
+ * KV head h / G. K/V are never expanded to Hq heads (the repeat_kv of section
+ * "图优化与算子融合" is never materialised).
+ *
+ * Paged cache (same page, section "动态形状与KV Cache管理"; page
+ * "TensorRT-LLM与TensorRT核心差异解析" section 4.2.2): the caller owns a pool
+ * of fixed-size pages and passes, per call, the physical page ids of each
+ * sequence. Token t of sequence b lives in physical page page_table[b][t / P]
+ * at slot t % P. Pool layout, for K and for V separately:
+ *     cache[num_pages][Hkv][P][D]      (one (page, kv head) block is P*D
+ *                                        contiguous elements)
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer owned by the caller. The library never
+ *     allocates, frees or synchronises, and keeps no state between calls, so
+ *     calls from several host threads are safe.
+ *   - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) and runs asynchronously; the return value reports
+ *     host-side argument validation and the launch only. A device fault (for
+ *     example a page id outside [0, num_pages)) surfaces at the caller's next
+ *     synchronisation.
+ *   - Tensors are dense and row-major in the layouts given below.
+ *   - page_table and context_lens are int32. Only the first ceil(T_b / P)
+ *     entries of a page-table row are read; later entries may hold anything.
+ *     Cache slots that no live token owns are never read into the result
+ *     (they may hold NaN).
+ *   - Supported: D in {64, 128}; P == 16; G in {1, 2, 4, 8, 16, 32} for
+ *     decode and {1, 2, 4, 8} for prefill; dtype GQA_F32 or GQA_BF16 for
+ *     decode, GQA_BF16 for prefill. Accumulation is fp32 throughout.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0, ... */
+  GQA_ERR_UNSUPPORTED = 2, /* valid but not built: D, P, G or dtype outside the supported set */
+  GQA_ERR_LAUNCH = 3       /* the HIP runtime refused the kernel launch */
+} gqa_status;
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+/*
+ * Single-token decode over a paged cache, optionally split along the context
+ * (NumSplits: page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践",
+ * section "核心参数调优：PackGQA与NumSplits的协同舞蹈").
+ *
+ *   q            [B][Hq][D]              dtype
+ *   k_cache      [num_pages][Hkv][P][D]  dtype
+ *   v_cache      [num_pages][Hkv][P][D]  dtype
+ *   page_table   [B][max_pages]          int32 physical page ids
+ *   context_lens [B]                     int32 T_b; clamped to max_pages*P;
+ *                                        T_b <= 0 gives a zero output
+ *   out          [B][Hq][D]              dtype; out[b][h] = softmax(scale *
+ *                                        q[b][h] . K_b^T) V_b over tokens
+ *                                        0 .. T_b-1 (no mask)
+ *   ws_o, ws_lse fp32 [B][Hq][num_splits][D] and [B][Hq][num_splits];
+ *                may be NULL iff num_splits == 1.
+ *   num_splits   NS >= 1. Split s of sequence b covers logical pages
+ *                [s*c, min((s+1)*c, np_b)), c = ceil(np_b / NS),
+ *                np_b = ceil(T_b / P). With NS > 1 the kernel writes, per
+ *                split, the normalised partial output (ws_o) and the
+ *                natural-log log-sum-exp of the split's scaled scores
+ *                (ws_lse; -inf and a zero row for an empty split), then
+ *                gqa_combine_splits runs on the same stream and writes out.
+ *   scale        multiplier of q.k (1/sqrt(D) for standard attention).
+ *
+ * Returns GQA_OK, or an error code with nothing enqueued.
+ */
+int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* page_table, const int32_t* context_lens, void* out,
+                     float* ws_o, float* ws_lse, int B, int Hq, int Hkv, int D, int P,
+                     int max_pages, int num_pages, int num_splits, float scale, int dtype,
+                     void* stream);
+
+/*
+ * Causal prefill of S new tokens per sequence, with the new K/V appended to
+ * the paged cache (page "TensorRT对Grouped Query Attention的支持进展",
+ * section "动态形状与KV Cache管理": prefill fills the cache that decode then
+ * grows). Causal mask as named in the caption of Figure 2 of page
+ * "解锁GQA性能潜力：从批量大小敏感性到高效优化实践": row i (position i of
+ * 0..S-1) attends keys 0..i.
+ *
+ *   q          [B][S][Hq][D]   bf16
+ *   k, v       [B][S][Hkv][D]  bf16, the new tokens at positions 0..S-1
+ *   k_cache,   [num_pages][Hkv][P][D] bf16; on return (stream order) slot
+ *   v_cache    j % P of page page_table[b][j / P] holds k[b][j] / v[b][j]
+ *              for every j < S, copied bit for bit; nothing else is written.
+ *   page_table [B][max_pages] int32, first ceil(S/P) entries valid per row;
+ *              requires max_pages * P >= S. Pages of different sequences
+ *              must be distinct.
+ *   out        [B][S][Hq][D]   bf16 (round to nearest even)
+ */
+int gqa_prefill_causal(const void* q, const void* k, const void* v, void* k_cache,
+                       void* v_cache, const int32_t* page_table, void* out, int B, int S,
+                       int Hq, int Hkv, int D, int P, int max_pages, int num_pages,
+                       float scale, int dtype, void* stream);
+
+/*
+ * Merge split partials: M = max_s lse_s, w_s = exp(lse_s - M),
+ * out = sum_s w_s o_s / sum_s w_s; a row whose splits are all -inf is zero.
+ *   ws_o [B][Hq][num_splits][D] fp32, ws_lse [B][Hq][num_splits] fp32
+ *   (natural log), out [B][Hq][D] in out_dtype.
+ */
+int gqa_combine_splits(const float* ws_o, const float* ws_lse, void* out, int B, int Hq, int D,
+                       int num_splits, int out_dtype, void* stream);
+
+/* Host-only helpers (no GPU access). */
+size_t gqa_decode_workspace_bytes(int B, int Hq, int D, int num_splits); /* ws_o + ws_lse */
+const char* gqa_status_string(int status);
+int gqa_validate_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, const int32_t* context_lens, const void* out,
+                        const float* ws_o, const float* ws_lse, int B, int Hq, int Hkv, int D,
+                        int P, int max_pages, int num_pages, int num_splits, float scale,
+                        int dtype);
+int gqa_validate_prefill(const void* q, const void* k, const void* v, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const void* out, int B,
+                         int S, int Hq, int Hkv, int D, int P, int max_pages, int num_pages,
+                         float scale, int dtype);
+int gqa_validate_combine(const float* ws_o, const float* ws_lse, const void* out, int B, int Hq,
+                         int D, int num_splits, int out_dtype);
+
+/*
+ * Test-only: copy the live tokens of a paged cache to a contiguous buffer,
+ * dst[b][t][kvh][:] = cache[page_table[b][t / P]][kvh][t % P][:] for
+ * t < min(context_lens[b], max_pages*P); dst is [B][max_pages*P][Hkv][D] and
+ * rows t >= T_b are left untouched. Bit-exact copy of the indexing that the
+ * attention kernels use.
+ */
+int gqa_gather_paged(const void* cache, const int32_t* page_table, const int32_t* context_lens,
+                     void* dst, int B, int Hkv, int D, int P, int max_pages, int num_pages,
+                     int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

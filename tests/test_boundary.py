@@ -1,0 +1,148 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load, export every function that include/gqa.h declares, and
+reject invalid arguments on the host with the documented status codes before
+anything is enqueued (so these calls never touch a device).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_paged_kv_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(g.LIB_PATH):
+        from gqa_paged_kv_amd import build
+        build.build()
+    return g.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("gqa_decode_paged", "gqa_prefill_causal", "gqa_combine_splits"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(g.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings(lib):
+    assert g.status_string(0) == "ok"
+    assert "invalid" in g.status_string(1)
+    assert "unsupported" in g.status_string(2)
+    assert "launch" in g.status_string(3)
+
+
+def test_workspace_bytes(lib):
+    assert g.workspace_bytes(8, 32, 128, 16) == 8 * 32 * 16 * (128 + 1) * 4
+    assert g.workspace_bytes(0, 32, 128, 16) == 0
+
+
+def _vd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, pt=FAKE, lens=FAKE, out=FAKE, wo=None, wl=None, B=2, Hq=8,
+             Hkv=2, D=128, P=16, max_pages=4, num_pages=8, ns=1, scale=0.125, dtype=g.BF16)
+    a.update(kw)
+    return lib.gqa_validate_decode(a["q"], a["k"], a["v"], a["pt"], a["lens"], a["out"], a["wo"],
+                                   a["wl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["P"],
+                                   a["max_pages"], a["num_pages"], a["ns"], a["scale"], a["dtype"])
+
+
+def test_decode_validation_rules(lib):
+    assert _vd(lib) == g.OK
+    assert _vd(lib, dtype=g.F32, D=64) == g.OK
+    for G in (1, 2, 4, 8, 16, 32):
+        assert _vd(lib, Hq=32, Hkv=32 // G) == g.OK
+    # invalid arguments
+    assert _vd(lib, Hq=6, Hkv=4) == g.ERR_INVALID_ARG  # non-uniform grouping
+    for k in ("B", "Hq", "Hkv", "D", "P", "max_pages", "num_pages"):
+        assert _vd(lib, **{k: 0}) == g.ERR_INVALID_ARG, k
+        assert _vd(lib, **{k: -3}) == g.ERR_INVALID_ARG, k
+    for k in ("q", "k", "v", "pt", "lens", "out"):
+        assert _vd(lib, **{k: None}) == g.ERR_INVALID_ARG, k
+    assert _vd(lib, ns=0) == g.ERR_INVALID_ARG
+    assert _vd(lib, ns=4) == g.ERR_INVALID_ARG  # NS > 1 without workspace
+    assert _vd(lib, ns=4, wo=FAKE, wl=FAKE) == g.OK
+    assert _vd(lib, ns=4, wo=FAKE) == g.ERR_INVALID_ARG
+    assert _vd(lib, scale=float("nan")) == g.ERR_INVALID_ARG
+    assert _vd(lib, scale=float("inf")) == g.ERR_INVALID_ARG
+    assert _vd(lib, dtype=7) == g.ERR_INVALID_ARG
+    # valid but not built
+    assert _vd(lib, D=96) == g.ERR_UNSUPPORTED
+    assert _vd(lib, P=32) == g.ERR_UNSUPPORTED
+    assert _vd(lib, Hq=48, Hkv=1) == g.ERR_UNSUPPORTED  # G = 48
+    assert _vd(lib, Hq=12, Hkv=4) == g.ERR_UNSUPPORTED  # G = 3
+    assert _vd(lib, ns=1000, wo=FAKE, wl=FAKE) == g.ERR_UNSUPPORTED
+
+
+def _vp(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, pt=FAKE, out=FAKE, B=4, S=2048, Hq=32,
+             Hkv=8, D=128, P=16, max_pages=128, num_pages=600, scale=0.088, dtype=g.BF16)
+    a.update(kw)
+    return lib.gqa_validate_prefill(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["pt"], a["out"],
+                                    a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["P"],
+                                    a["max_pages"], a["num_pages"], a["scale"], a["dtype"])
+
+
+def test_prefill_validation_rules(lib):
+    assert _vp(lib) == g.OK
+    assert _vp(lib, max_pages=127) == g.ERR_INVALID_ARG  # max_pages * P < S
+    assert _vp(lib, S=0) == g.ERR_INVALID_ARG
+    assert _vp(lib, Hq=30) == g.ERR_INVALID_ARG
+    for k in ("q", "k", "v", "kc", "vc", "pt", "out"):
+        assert _vp(lib, **{k: None}) == g.ERR_INVALID_ARG, k
+    assert _vp(lib, dtype=g.F32) == g.ERR_UNSUPPORTED
+    assert _vp(lib, Hq=32, Hkv=2) == g.ERR_UNSUPPORTED  # G = 16 not built for prefill
+    assert _vp(lib, D=64) == g.ERR_UNSUPPORTED
+    assert _vp(lib, P=8) == g.ERR_UNSUPPORTED
+
+
+def test_combine_validation_rules(lib):
+    v = lib.gqa_validate_combine
+    assert v(FAKE, FAKE, FAKE, 4, 32, 128, 8, g.BF16) == g.OK
+    assert v(None, FAKE, FAKE, 4, 32, 128, 8, g.BF16) == g.ERR_INVALID_ARG
+    assert v(FAKE, FAKE, FAKE, 4, 32, 128, 0, g.BF16) == g.ERR_INVALID_ARG
+    assert v(FAKE, FAKE, FAKE, 4, 32, 100, 8, g.BF16) == g.ERR_UNSUPPORTED
+    assert v(FAKE, FAKE, FAKE, 4, 32, 128, 8, 5) == g.ERR_INVALID_ARG
+
+
+def test_entry_points_reject_before_enqueueing(lib):
+    # Invalid calls return their status without touching the device.
+    st = lib.gqa_decode_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 2, 6, 4, 128, 16,
+                              4, 8, 1, 0.1, g.BF16, None)
+    assert st == g.ERR_INVALID_ARG
+    st = lib.gqa_prefill_causal(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 8, 2, 128, 16,
+                                4, 8, 0.1, g.F32, None)
+    assert st == g.ERR_UNSUPPORTED
+    st = lib.gqa_combine_splits(FAKE, None, FAKE, 1, 8, 128, 2, g.BF16, None)
+    assert st == g.ERR_INVALID_ARG
+    st = lib.gqa_gather_paged(FAKE, FAKE, FAKE, FAKE, 1, 2, 96, 16, 4, 8, g.BF16, None)
+    assert st == g.ERR_UNSUPPORTED
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "gqa_paged_kv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in text.lower().replace("oracles", ""), f

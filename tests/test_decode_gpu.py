@@ -1,0 +1,222 @@
+"""GPU parity of paged GQA decode, split/combine and gather against the float64 oracle.
+
+Every case is seeded and synthetic (synth/); the oracle runs on the CPU on the
+same tensors the kernels read.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import assert_close, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _ref(x):
+    c = x.to("cpu")
+    return oracle.decode_paged(c.q, c.k_cache, c.v_cache, c.page_table, c.context_lens, c.scale)
+
+
+def _run(g, x, ns=1):
+    out = g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, num_splits=ns,
+                         scale=x.scale)
+    _sync()
+    return out
+
+
+# ---------------------------------------------------------------- workload 1
+
+@pytest.mark.parametrize("ns", [1, 2, 4, 16])
+def test_config1_tiny_fp32(gpu_lib, ns):
+    print(f"[decode] config1 fp32 ns={ns}", flush=True)
+    x = synth.config1(device=DEV)
+    out = _run(gpu_lib, x, ns)
+    assert_close(out, _ref(x), "f32", f"config1 ns={ns}")
+
+
+# ---------------------------------------------------- small shapes, every instance
+
+SMALL = [
+    # dtype, D, Hq, Hkv, lens
+    ("bf16", 128, 8, 2, [1, 77, 300]),
+    ("bf16", 128, 32, 8, [16, 64, 65, 129]),
+    ("bf16", 128, 4, 4, [5, 200]),
+    ("bf16", 128, 32, 1, [63, 190]),
+    ("bf16", 128, 32, 2, [33, 250]),
+    ("bf16", 128, 16, 2, [100]),
+    ("bf16", 64, 8, 2, [1, 130, 257]),
+    ("bf16", 64, 32, 1, [77, 511]),
+    ("bf16", 64, 16, 1, [40]),
+    ("f32", 64, 8, 2, [1, 100, 255]),
+    ("f32", 64, 32, 1, [31, 97]),
+    ("f32", 128, 8, 2, [3, 33, 150]),
+    ("f32", 128, 32, 4, [70]),
+    ("f32", 128, 16, 1, [45, 46]),
+    ("f32", 64, 2, 1, [18]),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-D{c[1]}-{c[2]}x{c[3]}")
+@pytest.mark.parametrize("ns", [1, 3])
+def test_small_shapes(gpu_lib, case, ns):
+    dtype, D, hq, hkv, lens = case
+    print(f"[decode] small {case} ns={ns}", flush=True)
+    x = synth.decode_inputs(len(lens), hq, hkv, D, 16, lens, dtype,
+                            seed=D + 7 * hq + 13 * hkv + len(lens), device=DEV)
+    out = _run(gpu_lib, x, ns)
+    assert_close(out, _ref(x), dtype, f"{case} ns={ns}")
+
+
+def test_empty_and_single_token_sequences(gpu_lib):
+    print("[decode] empty/single", flush=True)
+    x = synth.decode_inputs(4, 8, 2, 128, 16, [0, 1, 0, 17], "bf16", seed=5, device=DEV)
+    for ns in (1, 4):
+        out = _run(gpu_lib, x, ns)
+        assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+        ref = _ref(x)
+        # one token: the output is exactly that token's V row (rounded to bf16 it is itself)
+        pt = x.page_table.cpu()
+        v0 = x.v_cache[int(pt[1, 0]), :, 0].cpu()
+        assert torch.equal(out[1].cpu(), v0.repeat_interleave(4, 0))
+        assert_close(out, ref, "bf16", f"empty/single ns={ns}")
+
+
+def test_context_longer_than_table_is_clamped(gpu_lib):
+    print("[decode] clamp", flush=True)
+    x = synth.decode_inputs(2, 8, 2, 128, 16, [40, 64], "bf16", seed=6, device=DEV)
+    lens_big = torch.tensor([40, 10_000], dtype=torch.int32, device=DEV)  # row 1 table holds 4 pages
+    out = gpu_lib.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, lens_big, scale=x.scale)
+    _sync()
+    ref = _ref(x)  # T_1 = 64 = max_pages * P
+    assert_close(out, ref, "bf16", "clamped")
+
+
+# ---------------------------------------------------------------- workload 2
+
+@pytest.fixture(scope="module")
+def cfg2():
+    x = synth.config2(device=DEV)
+    return x, _ref(x)
+
+
+@pytest.mark.parametrize("ns", [1, 4, 8, 16])
+def test_config2_paged_bf16(gpu_lib, cfg2, ns):
+    print(f"[decode] config2 ns={ns}", flush=True)
+    x, ref = cfg2
+    out = _run(gpu_lib, x, ns)
+    assert_close(out, ref, "bf16", f"config2 ns={ns}")
+
+
+def test_config2_deterministic_and_page_permutation_invariant(gpu_lib, cfg2):
+    print("[decode] config2 determinism / permutation", flush=True)
+    x, _ = cfg2
+    a = _run(gpu_lib, x, 8)
+    b = _run(gpu_lib, x, 8)
+    assert torch.equal(a, b)
+    n = x.k_cache.shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(77)).to(DEV)
+    k2 = torch.empty_like(x.k_cache)
+    v2 = torch.empty_like(x.v_cache)
+    k2[perm] = x.k_cache
+    v2[perm] = x.v_cache
+    pt2 = x.page_table.clone()
+    live = pt2 >= 0
+    pt2[live] = perm[pt2[live].long()].to(torch.int32)
+    for ns in (1, 8):
+        base = _run(gpu_lib, x, ns)
+        moved = gpu_lib.decode_paged(x.q, k2, v2, pt2, x.context_lens, num_splits=ns, scale=x.scale)
+        _sync()
+        assert torch.equal(base, moved), f"ns={ns}"
+
+
+def test_poison_does_not_leak(gpu_lib):
+    print("[decode] poison", flush=True)
+    x = synth.decode_inputs(3, 32, 8, 128, 16, [37, 300, 16], "bf16", seed=8, device=DEV,
+                            poison=True)
+    clean_k = torch.nan_to_num(x.k_cache, nan=0.0)
+    clean_v = torch.nan_to_num(x.v_cache, nan=0.0)
+    pt_far = x.page_table.clone()
+    pt_far[pt_far < 0] = 2**30  # entries past the last page: never read
+    for ns in (1, 3):
+        a = _run(gpu_lib, x, ns)
+        b = gpu_lib.decode_paged(x.q, clean_k, clean_v, pt_far, x.context_lens, num_splits=ns,
+                                 scale=x.scale)
+        _sync()
+        assert torch.isfinite(a.float()).all()
+        assert torch.equal(a, b), f"ns={ns}"
+
+
+# ---------------------------------------------------------------- workload 4
+
+@pytest.mark.parametrize("B", synth.CONFIG4_BATCHES)
+def test_config4_long_context_splits(gpu_lib, B):
+    print(f"[decode] config4 B={B}", flush=True)
+    x = synth.config4(B, device=DEV)
+    ref = _ref(x)
+    outs = {}
+    for ns in synth.CONFIG4_SPLITS:
+        outs[ns] = _run(gpu_lib, x, ns)
+        assert_close(outs[ns], ref, "bf16", f"config4 B={B} ns={ns}")
+
+
+# ---------------------------------------------------------------- workload 5
+
+@pytest.mark.parametrize("Hkv", synth.CONFIG5_KV_HEADS)
+@pytest.mark.parametrize("B", synth.CONFIG5_BATCHES)
+def test_config5_sweep(gpu_lib, B, Hkv):
+    print(f"[decode] config5 B={B} Hkv={Hkv}", flush=True)
+    x = synth.config5(B, Hkv, device=DEV)
+    out = _run(gpu_lib, x, 1)
+    rng = np.random.default_rng(B * 100 + Hkv)
+    n_rows = min(B * 32, 48)
+    flat = rng.choice(B * 32, size=n_rows, replace=False)
+    rows = [(int(i) // 32, int(i) % 32) for i in flat]
+    c = x.to("cpu")
+    ref = oracle.decode_paged_rows(c.q, c.k_cache, c.v_cache, c.page_table, c.context_lens,
+                                   c.scale, rows)
+    got = np.stack([to_f64(out[b, h]) for (b, h) in rows])
+    want = np.stack([ref[r] for r in rows])
+    assert_close(got, want, "bf16", f"config5 B={B} Hkv={Hkv}")
+
+
+# ---------------------------------------------------------------- gather / combine
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+def test_gather_is_bit_exact(gpu_lib, dtype, D):
+    print(f"[gather] {dtype} D={D}", flush=True)
+    x = synth.decode_inputs(3, 8, 4, D, 16, [5, 48, 131], dtype, seed=9, device=DEV)
+    dst = gpu_lib.gather_paged(x.k_cache, x.page_table, x.context_lens)
+    _sync()
+    c = x.to("cpu")
+    want = oracle.gather_paged(c.k_cache, c.page_table, c.context_lens, 16)
+    dst = dst.cpu()
+    for b in range(3):
+        T = int(c.context_lens[b])
+        assert torch.equal(dst[b, :T].view(torch.int16 if dtype == "bf16" else torch.int32),
+                           want[b].view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_combine_standalone(gpu_lib, out_dtype):
+    print(f"[combine] {out_dtype}", flush=True)
+    g = torch.Generator().manual_seed(3)
+    B, Hq, NS, D = 3, 8, 6, 128
+    o = torch.randn(B, Hq, NS, D, generator=g)
+    lse = torch.randn(B, Hq, NS, generator=g) * 5
+    lse[0, 0, :] = -float("inf")         # all splits empty -> zero
+    lse[0, 1, 1:] = -float("inf")        # one live split
+    lse[1, 2, 3] = 80.0                  # one dominant split
+    lse[2, :, ::2] = -float("inf")       # empty splits interleaved
+    out = gpu_lib.combine_splits(o.to(DEV), lse.to(DEV), out_dtype)
+    _sync()
+    ref = oracle.combine_splits(o, lse)
+    assert torch.all(out[0, 0] == 0)
+    assert_close(out, ref, "f32" if out_dtype == torch.float32 else "bf16", "combine")
