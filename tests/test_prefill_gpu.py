@@ -1,0 +1,97 @@
+"""GPU parity of causal GQA prefill (bf16 MFMA) and its paged KV append."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import assert_close, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(g, x):
+    out = g.prefill_causal(x.q, x.k, x.v, x.k_cache, x.v_cache, x.page_table, scale=x.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_append(x, k_before, v_before):
+    """Cache after append equals the oracle's scatter, bit for bit (NaN pads included)."""
+    pt = x.page_table.cpu()
+    want_k = oracle.append_paged(k_before, x.k.cpu(), pt, k_before.shape[2])
+    want_v = oracle.append_paged(v_before, x.v.cpu(), pt, v_before.shape[2])
+    assert torch.equal(x.k_cache.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(x.v_cache.cpu().view(torch.int16), want_v.view(torch.int16))
+
+
+SMALL = [
+    # B, S, Hq, Hkv
+    (1, 1, 4, 1),
+    (2, 33, 8, 2),
+    (2, 64, 8, 2),
+    (1, 100, 16, 4),
+    (2, 257, 8, 2),
+    (1, 300, 4, 4),
+    (1, 190, 8, 4),
+    (1, 129, 16, 2),
+    (2, 520, 32, 8),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}-S{}-{}x{}".format(*c))
+def test_prefill_small_shapes(gpu_lib, case):
+    B, S, hq, hkv = case
+    print(f"[prefill] small {case}", flush=True)
+    x = synth.prefill_inputs(B, S, hq, hkv, 128, 16, seed=S + hq + 10 * hkv, device=DEV)
+    kb, vb = x.k_cache.cpu(), x.v_cache.cpu()
+    out = _run(gpu_lib, x)
+    c = x.to("cpu")
+    ref = oracle.prefill_causal(c.q, c.k, c.v, c.scale)
+    assert_close(out, ref, "bf16", f"prefill {case}")
+    _check_append(x, kb, vb)
+
+
+def test_prefill_row0_is_v0_and_identical_keys_give_running_mean(gpu_lib):
+    print("[prefill] closed forms", flush=True)
+    x = synth.prefill_inputs(1, 130, 8, 2, 128, 16, seed=4, device=DEV)
+    x.k[:] = 0.25  # identical keys: row i = mean of V[0..i]
+    out = _run(gpu_lib, x)
+    v = to_f64(x.v)
+    # row 0 sees one key: exactly V[0] (p = 1, l = 1)
+    for h in range(8):
+        assert torch.equal(out[0, 0, h].cpu(), x.v[0, 0, h // 4].cpu())
+    running = np.cumsum(v[0], axis=0) / np.arange(1, 131)[:, None, None]
+    want = np.repeat(running, 4, axis=1)
+    assert_close(out[0], want, "bf16", "running mean")
+
+
+@pytest.fixture(scope="module")
+def cfg3():
+    x = synth.config3(device=DEV)
+    kb, vb = x.k_cache.cpu(), x.v_cache.cpu()
+    return x, kb, vb
+
+
+def test_config3_prefill_sampled_heads_and_append(gpu_lib, cfg3):
+    print("[prefill] config3", flush=True)
+    x, kb, vb = cfg3
+    out = _run(gpu_lib, x)
+    _check_append(x, kb, vb)
+    c = x.to("cpu")
+    rows = [(b, h) for b in range(4) for h in (b, 8 + 3 * b, 31 - b)]  # every b, spread heads
+    ref = oracle.prefill_causal_rows(c.q, c.k, c.v, c.scale, rows)
+    got = np.stack([to_f64(out[b, :, h]) for (b, h) in rows])
+    want = np.stack([ref[r] for r in rows])
+    assert_close(got, want, "bf16", "config3 sampled heads")
+
+
+def test_config3_deterministic(gpu_lib, cfg3):
+    print("[prefill] config3 determinism", flush=True)
+    x, _, _ = cfg3
+    a = _run(gpu_lib, x)
+    b = _run(gpu_lib, x)
+    assert torch.equal(a, b)
+    assert torch.isfinite(a.float()).all()
