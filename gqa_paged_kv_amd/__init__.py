@@ -26,6 +26,8 @@ _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16}
 _p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "gqa_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _p, _p] + [_i] * 8 + [_f, _i, _p]),
+    "gqa_decode_paged_balanced": (_i, [_p] * 7 + [_sz] + [_i] * 7 + [_f, _i, _p]),
+    "gqa_decode_balanced_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "gqa_prefill_causal": (_i, [_p] * 7 + [_i] * 8 + [_f, _i, _p]),
     "gqa_combine_splits": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "gqa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -34,6 +36,8 @@ SIGNATURES = {
     "gqa_validate_prefill": (_i, [_p] * 7 + [_i] * 8 + [_f, _i]),
     "gqa_validate_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _i]),
     "gqa_gather_paged": (_i, [_p, _p, _p, _p] + [_i] * 7 + [_p]),
+    "gqa_bench_stream_read": (_i, [_p, _sz, _p, _i, _i, _p]),
+    "gqa_bench_mfma_bf16": (_i, [_p, _i, _i, _p]),
 }
 
 _lib = None
@@ -142,6 +146,47 @@ def decode_paged(q, k_cache, v_cache, page_table, context_lens, num_splits: int 
     return out
 
 
+def balanced_workspace(B: int, Hq: int, Hkv: int, D: int, device):
+    """Device scratch for decode_paged_balanced (uint8 tensor, 256-byte aligned)."""
+    n = int(load().gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode_paged_balanced(q, k_cache, v_cache, page_table, context_lens,
+                          scale: float | None = None, out=None, workspace=None):
+    """Paged GQA decode with the library's balanced work partition; returns out [B][Hq][D]."""
+    lib = load()
+    _need(q, "q", dim=3)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    if page_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("page_table / context_lens batch mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype, 3)
+    if workspace is None:
+        workspace = balanced_workspace(B, Hq, Hkv, D, q.device)
+    _need(workspace, "workspace")
+    st = lib.gqa_decode_paged_balanced(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                       _ptr(context_lens), _ptr(out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), B, Hq, Hkv,
+                                       D, P, page_table.shape[1], num_pages, scale,
+                                       _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st, "gqa_decode_paged_balanced")
+    return out
+
+
 def combine_splits(ws_o, ws_lse, out_dtype=torch.bfloat16, out=None):
     """LSE merge of split partials; returns out [B][Hq][D]."""
     lib = load()
@@ -194,3 +239,16 @@ def gather_paged(cache, page_table, context_lens, dst=None):
                               _stream(cache.device))
     _check(st, "gqa_gather_paged")
     return dst
+
+
+def bench_stream_read(src, sink, blocks_per_cu: int = 8, unroll: int = 8):
+    """Bench-only: stream-read all of ``src`` (a device tensor) with 128-bit loads."""
+    st = load().gqa_bench_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                      blocks_per_cu, unroll, _stream(src.device))
+    _check(st, "gqa_bench_stream_read")
+
+
+def bench_mfma_bf16(sink, blocks: int, iters: int):
+    """Bench-only: back-to-back bf16 32x32x16 MFMAs; flops = blocks * 8 * iters * 32768."""
+    st = load().gqa_bench_mfma_bf16(_ptr(sink), blocks, iters, _stream(sink.device))
+    _check(st, "gqa_bench_mfma_bf16")

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqa.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["api.hip", "decode.hip", "aux_kernels.hip", "prefill.hip"]
+HIP_SOURCES = ["api.hip", "decode.hip", "decode_balanced.hip", "aux_kernels.hip", "prefill.hip",
+               "ceiling.hip"]
 CPP_SOURCES = ["validate.cpp"]
 
 HIPCC_FLAGS = [

@@ -16,9 +16,14 @@ int launch_gather(const void* cache, const int32_t* pt, const int32_t* lens, voi
                   int Hkv, int D, int P, int max_pages, int dtype, hipStream_t s);
 int launch_append(const void* src, const int32_t* pt, void* cache, int B, int S, int Hkv, int D,
                   int P, int max_pages, int elem_bytes, hipStream_t s);
+int launch_decode_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
+                           const int32_t* lens, void* out, void* ws, int B, int Hq, int Hkv,
+                           int D, int max_pages, float scale, int dtype, hipStream_t s);
 int launch_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s);
 }  // namespace gqa
+
+extern "C" int gqa_balanced_auto_splits(int B, int Hkv);
 
 extern "C" {
 
@@ -35,6 +40,32 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                                 B, Hq, Hkv, D, max_pages, num_splits, scale, dtype, s);
   if (st != GQA_OK || num_splits == 1) return st;
   return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, num_splits, dtype, s);
+}
+
+int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* context_lens, void* out,
+                              void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                              int D, int P, int max_pages, int num_pages, float scale, int dtype,
+                              void* stream) {
+  int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
+                               nullptr, B, Hq, Hkv, D, P, max_pages, num_pages, 1, scale, dtype);
+  if (st != GQA_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
+  if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (Hq / Hkv <= 8)
+    return gqa::launch_decode_balanced(q, k_cache, v_cache, page_table, context_lens, out,
+                                       workspace, B, Hq, Hkv, D, max_pages, scale, dtype, s);
+  const int ns = gqa_balanced_auto_splits(B, Hkv);
+  if (ns == 1)
+    return gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
+                                    nullptr, B, Hq, Hkv, D, max_pages, 1, scale, dtype, s);
+  float* ws_o = (float*)workspace;
+  float* ws_lse = ws_o + (size_t)B * Hq * ns * D;
+  st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
+                                B, Hq, Hkv, D, max_pages, ns, scale, dtype, s);
+  if (st != GQA_OK) return st;
+  return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, ns, dtype, s);
 }
 
 int gqa_combine_splits(const float* ws_o, const float* ws_lse, void* out, int B, int Hq, int D,

@@ -73,8 +73,24 @@ int gqa_validate_decode(const void* q, const void* k_cache, const void* v_cache,
   if (st != GQA_OK) return st;
   if (!supported_decode_group(Hq / Hkv)) return GQA_ERR_UNSUPPORTED;
   if (num_splits > kMaxSplits) return GQA_ERR_UNSUPPORTED;
-  if ((int64_t)Hkv * num_splits > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)Hkv * num_splits > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;  // grid.x
   return GQA_OK;
+}
+
+// Split count used by the balanced entry point when G >= 16 (the LDS-staged split path).
+int gqa_balanced_auto_splits(int B, int Hkv) {
+  const long units = (long)B * Hkv;
+  long ns = (1024 + units - 1) / units;
+  return (int)(ns < 1 ? 1 : (ns > 16 ? 16 : ns));
+}
+
+size_t gqa_decode_balanced_workspace_bytes(int B, int Hq, int Hkv, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
+  const size_t G = (size_t)(Hq / Hkv);
+  // persistent path: 4096 waves x 2 slots x G x (D + 1) floats, then B + 1 ints
+  const size_t stream_bytes = (size_t)4096 * 2 * G * (D + 1) * sizeof(float) + (size_t)(B + 1) * 4;
+  const size_t split_bytes = gqa_decode_workspace_bytes(B, Hq, D, gqa_balanced_auto_splits(B, Hkv));
+  return stream_bytes > split_bytes ? stream_bytes : split_bytes;
 }
 
 int gqa_validate_prefill(const void* q, const void* k, const void* v, const void* k_cache,

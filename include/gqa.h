@@ -90,6 +90,29 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                      void* stream);
 
 /*
+ * Same result as gqa_decode_paged, with the work partition chosen by the library so
+ * that unequal context lengths do not leave the GPU idle: the batch's
+ * (sequence, KV head, page) items are cut into equal contiguous shares, one per
+ * resident wave; a (sequence, KV head) unit cut by a share boundary is finished from
+ * its pieces with the log-sum-exp merge of gqa_combine_splits (the NumSplits
+ * decomposition of page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
+ * "核心参数调优：PackGQA与NumSplits的协同舞蹈"). For G >= 16 it runs the split path with
+ * an automatic split count.
+ *
+ *   workspace        device scratch of at least
+ *                    gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D) bytes, 256-byte
+ *                    aligned, owned by the caller; contents need no initialisation and
+ *                    are overwritten. Calls that share a workspace must not overlap.
+ *   other arguments  as for gqa_decode_paged.
+ * Enqueues three kernels (page-count prefix sum, decode, fix-up) on `stream`.
+ */
+int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* context_lens, void* out,
+                              void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                              int D, int P, int max_pages, int num_pages, float scale, int dtype,
+                              void* stream);
+
+/*
  * Causal prefill of S new tokens per sequence, with the new K/V appended to
  * the paged cache (page "TensorRT对Grouped Query Attention的支持进展",
  * section "动态形状与KV Cache管理": prefill fills the cache that decode then
@@ -123,6 +146,7 @@ int gqa_combine_splits(const float* ws_o, const float* ws_lse, void* out, int B,
 
 /* Host-only helpers (no GPU access). */
 size_t gqa_decode_workspace_bytes(int B, int Hq, int D, int num_splits); /* ws_o + ws_lse */
+size_t gqa_decode_balanced_workspace_bytes(int B, int Hq, int Hkv, int D);  /* 0 if invalid */
 const char* gqa_status_string(int status);
 int gqa_validate_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* page_table, const int32_t* context_lens, const void* out,

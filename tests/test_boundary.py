@@ -14,7 +14,7 @@ import pytest
 import gqa_paged_kv_amd as g
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gqa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gqa.h", "gqa_bench.h")]
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
@@ -27,9 +27,9 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_three_entry_points():

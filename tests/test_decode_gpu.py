@@ -220,3 +220,91 @@ def test_combine_standalone(gpu_lib, out_dtype):
     ref = oracle.combine_splits(o, lse)
     assert torch.all(out[0, 0] == 0)
     assert_close(out, ref, "f32" if out_dtype == torch.float32 else "bf16", "combine")
+
+
+# ---------------------------------------------------------------- balanced partition
+
+def _run_bal(g, x):
+    out = g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
+                                  scale=x.scale)
+    _sync()
+    return out
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-D{c[1]}-{c[2]}x{c[3]}")
+def test_balanced_small_shapes(gpu_lib, case):
+    dtype, D, hq, hkv, lens = case
+    print(f"[balanced] small {case}", flush=True)
+    x = synth.decode_inputs(len(lens), hq, hkv, D, 16, lens, dtype,
+                            seed=D + 7 * hq + 13 * hkv + len(lens), device=DEV)
+    assert_close(_run_bal(gpu_lib, x), _ref(x), dtype, f"balanced {case}")
+
+
+def test_balanced_config1_and_empty_sequences(gpu_lib):
+    print("[balanced] config1 / empty", flush=True)
+    x = synth.config1(device=DEV)
+    assert_close(_run_bal(gpu_lib, x), _ref(x), "f32", "balanced config1")
+    y = synth.decode_inputs(5, 8, 2, 128, 16, [0, 1, 0, 17, 0], "bf16", seed=5, device=DEV)
+    out = _run_bal(gpu_lib, y)
+    for b in (0, 2, 4):
+        assert torch.all(out[b] == 0)
+    assert_close(out, _ref(y), "bf16", "balanced empty")
+
+
+def test_balanced_config2_parity_determinism_permutation(gpu_lib, cfg2):
+    print("[balanced] config2", flush=True)
+    x, ref = cfg2
+    a = _run_bal(gpu_lib, x)
+    assert_close(a, ref, "bf16", "balanced config2")
+    assert torch.equal(a, _run_bal(gpu_lib, x))
+    n = x.k_cache.shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(78)).to(DEV)
+    k2 = torch.empty_like(x.k_cache)
+    v2 = torch.empty_like(x.v_cache)
+    k2[perm] = x.k_cache
+    v2[perm] = x.v_cache
+    pt2 = x.page_table.clone()
+    live = pt2 >= 0
+    pt2[live] = perm[pt2[live].long()].to(torch.int32)
+    moved = gpu_lib.decode_paged_balanced(x.q, k2, v2, pt2, x.context_lens, scale=x.scale)
+    _sync()
+    assert torch.equal(a, moved)
+
+
+def test_balanced_poison(gpu_lib):
+    print("[balanced] poison", flush=True)
+    x = synth.decode_inputs(3, 32, 8, 128, 16, [37, 300, 16], "bf16", seed=8, device=DEV)
+    clean_k = torch.nan_to_num(x.k_cache, nan=0.0)
+    clean_v = torch.nan_to_num(x.v_cache, nan=0.0)
+    pt_far = x.page_table.clone()
+    pt_far[pt_far < 0] = 2**30
+    a = _run_bal(gpu_lib, x)
+    b = gpu_lib.decode_paged_balanced(x.q, clean_k, clean_v, pt_far, x.context_lens, scale=x.scale)
+    _sync()
+    assert torch.isfinite(a.float()).all()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("B", synth.CONFIG4_BATCHES)
+def test_balanced_config4(gpu_lib, B):
+    print(f"[balanced] config4 B={B}", flush=True)
+    x = synth.config4(B, device=DEV)
+    assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"balanced config4 B={B}")
+
+
+@pytest.mark.parametrize("Hkv", synth.CONFIG5_KV_HEADS)
+@pytest.mark.parametrize("B", (1, 16, 256))
+def test_balanced_config5(gpu_lib, B, Hkv):
+    print(f"[balanced] config5 B={B} Hkv={Hkv}", flush=True)
+    x = synth.config5(B, Hkv, device=DEV)
+    out = _run_bal(gpu_lib, x)
+    rng = np.random.default_rng(B * 100 + Hkv + 1)
+    n_rows = min(B * 32, 48)
+    flat = rng.choice(B * 32, size=n_rows, replace=False)
+    rows = [(int(i) // 32, int(i) % 32) for i in flat]
+    c = x.to("cpu")
+    ref = oracle.decode_paged_rows(c.q, c.k_cache, c.v_cache, c.page_table, c.context_lens,
+                                   c.scale, rows)
+    got = np.stack([to_f64(out[b, h]) for (b, h) in rows])
+    want = np.stack([ref[r] for r in rows])
+    assert_close(got, want, "bf16", f"balanced config5 B={B} Hkv={Hkv}")
