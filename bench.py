@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the paged GQA hot path on one MI355X.
 
-A step is one pass of the decode path (decode kernel + split combine) over the
-paged-decode workload: B=64 sequences, Hq=32, Hkv=8, D=128, page 16, context
+A step is one pass of the decode path (balanced decode kernel + fix-up merge,
+``gqa_decode_paged_balanced``; ``--splits NS`` times the split path instead) over
+the paged-decode workload: B=64 sequences, Hq=32, Hkv=8, D=128, page 16, context
 lengths uniform in [512, 4096], bf16, pages scattered by a seeded
 permutation. Inputs are resident in HBM before the timed region. ``value`` is
 algorithmic KV bytes (every live K and V row read once) per second of
@@ -29,7 +30,7 @@ import torch
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "decode KV GB/s (% HBM peak); prefill TFLOPS (% bf16 MFMA peak)"
-DEFAULT_SPLITS = 4
+DEFAULT_SPLITS = 0  # balanced partition (gqa_decode_paged_balanced)
 
 
 def kv_bytes(x) -> int:
@@ -61,25 +62,63 @@ def event_times(fn, n, stream, flush=None):
 
 
 def cpu_baseline_decode(x_cpu, budget_s=12.0):
+    """The float64 oracle over the decode workload's sequences, repeated until ~budget_s."""
     import oracle  # test infrastructure: the float64 CPU oracle, timed as a baseline only
     B = x_cpu.q.shape[0]
-    per_b = []
     t0w, t0c = time.perf_counter(), time.process_time()
     done_bytes = 0
-    b = 0
-    while time.perf_counter() - t0w < budget_s and b < B:
+    n = 0
+    while time.perf_counter() - t0w < budget_s:
+        b = n % B
         T = int(x_cpu.context_lens[b])
         oracle.decode_paged(x_cpu.q[b:b + 1], x_cpu.k_cache, x_cpu.v_cache,
                             x_cpu.page_table[b:b + 1], x_cpu.context_lens[b:b + 1], x_cpu.scale)
         done_bytes += 2 * T * x_cpu.k_cache.shape[1] * x_cpu.k_cache.shape[3] * 2
-        b += 1
+        n += 1
     wall = time.perf_counter() - t0w
     cpu = time.process_time() - t0c
-    return dict(value=done_bytes / wall / 1e9, unit="GB/s", cores=max(1, round(cpu / wall)),
-                kind="oracle",
-                sample=f"float64 oracle over the first {b} of {B} sequences of the decode "
-                       f"workload ({done_bytes / 1e6:.1f} MB of KV) in {wall:.1f} s",
+    return dict(value=round(done_bytes / wall / 1e9, 4), unit="GB/s",
+                cores=max(1, round(cpu / wall)), kind="oracle",
+                sample=f"float64 oracle, {n} sequence decodes of the decode workload "
+                       f"(all 32 heads each; {done_bytes / 1e6:.0f} MB of KV) in {wall:.1f} s",
                 host_cores=len(os.sched_getaffinity(0)))
+
+
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gqa_paged_kv_amd", "csrc")
+
+
+def measured_traffic(key):
+    """HBM bytes per call from the committed rocprofv3 PMC summary, or None if the kernel
+    sources changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(PROFILES, "traffic.json")))[key]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    except (OSError, KeyError, ValueError):
+        return None
+    if h.hexdigest()[:16] != rec["source_sha"]:
+        return None
+    return round(rec["hbm_bytes_per_call"])
+
+
+def ceilings(g, dev, stream):
+    """What this GPU reaches: a 2 GiB streaming read and a bf16 MFMA-only loop."""
+    src = torch.ones(2 * 2**30 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
+    f = lambda: g.bench_stream_read(src, sink, 8, 1)
+    f()
+    t_read = statistics.median(event_times(f, 10, stream))
+    del src
+    fs = torch.empty(1024 * 8, dtype=torch.float32, device=dev)
+    blocks, iters = 1024, 4096
+    h = lambda: g.bench_mfma_bf16(fs, blocks, iters)
+    h()
+    t_mfma = statistics.median(event_times(h, 5, stream))
+    return {"stream_read_gbs": round(2 * 2**30 / (t_read * 1e-3) / 1e9, 1),
+            "mfma_bf16_tflops": round(blocks * 8 * iters * 32768 / (t_mfma * 1e-3) / 1e12, 1)}
 
 
 def main():
@@ -110,14 +149,23 @@ def main():
 
     # ---------------- decode workload (inputs resident in HBM) ----------------
     x = synth.config2(device=dev)
-    ns = args.splits
+    ns = args.splits  # 0: the library's balanced partition
     out = torch.empty_like(x.q)
-    ws = g.alloc_workspace(x.q.shape[0], x.q.shape[1], x.q.shape[2], ns, dev) if ns > 1 else None
+    B, Hq, D = x.q.shape
+    Hkv = x.k_cache.shape[1]
+    if ns > 0:
+        ws = g.alloc_workspace(B, Hq, D, ns, dev) if ns > 1 else None
+    else:
+        ws = g.balanced_workspace(B, Hq, Hkv, D, dev)
     nbytes = kv_bytes(x)
 
     def step():
-        g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens, num_splits=ns,
-                       scale=x.scale, out=out, workspace=ws)
+        if ns > 0:
+            g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
+                           num_splits=ns, scale=x.scale, out=out, workspace=ws)
+        else:
+            g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
+                                    scale=x.scale, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -137,9 +185,11 @@ def main():
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (ev_avg * 1e-3) / 1e9
 
-    # same launch preceded by a 512 MiB write that evicts L2 and the Infinity Cache
-    scratch = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
-    flushed = event_times(step, 30, stream, flush=lambda: scratch.zero_())
+    # same launch preceded by a 1 GiB read that evicts L2 and the Infinity Cache
+    scratch = torch.ones(1024 * 2**20 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
+    flushed = event_times(step, 30, stream,
+                          flush=lambda: g.bench_stream_read(scratch, sink, 8, 1))
     flushed_med = statistics.median(flushed)
 
     line = {
@@ -158,7 +208,7 @@ def main():
         "config": {
             "workload": "paged GQA decode, B=64, Hq=32, Hkv=8, D=128, page 16, "
                         "T~U[512,4096], bf16, permuted pages",
-            "num_splits": ns,
+            "partition": "balanced (equal page shares per wave)" if ns == 0 else f"{ns} splits",
             "kv_bytes_per_step": nbytes,
             "total_context_tokens": int(x.context_lens.sum()),
         },
@@ -168,15 +218,17 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "decode_paged_kernel<bf16,128,4> + combine_kernel (one decode call)",
+            "traffic": measured_traffic("decode_balanced_bf16_B64_Hq32_Hkv8") if ns == 0 else None,
+            "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, calibrated)",
+            "kernel": ("balanced_kernel<bf16,128,4> + fixup_kernel (one decode call)" if ns == 0
+                       else "decode_regs_kernel<bf16,128,4> + combine_kernel (one decode call)"),
             "event_avg_us": round(ev_avg * 1e3, 2),
         },
         "decode_flushed": {
             "median_us": round(flushed_med * 1e3, 2),
             "gbs": round(nbytes / (flushed_med * 1e-3) / 1e9, 1),
             "frac": round(nbytes / (flushed_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "each launch preceded by a 512 MiB write (L2 + Infinity Cache evicted)",
+            "note": "each launch preceded by a 1 GiB streaming read (L2 + Infinity Cache evicted)",
         },
     }
     del scratch
@@ -205,11 +257,17 @@ def main():
             "tflops": round(tf, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": measured_traffic("prefill_causal_bf16_B4_S2048_Hq32_Hkv8"),
                          "kernel": "append_kernel x2 + prefill_causal_kernel<4> (one call)"},
             "flops_per_call": fl,
         }
         del p, pout
+
+    ceil = ceilings(g, dev, stream)
+    line["measured_ceiling"] = dict(ceil, decode_frac_of_read=round(achieved / ceil["stream_read_gbs"], 4))
+    if "prefill" in line:
+        line["prefill"]["frac_of_mfma_ceiling"] = round(
+            line["prefill"]["tflops"] / ceil["mfma_bf16_tflops"], 4)
 
     # ---------------- CPU baseline: the float64 oracle on the host ----------------
     if not args.no_cpu_baseline:
@@ -226,6 +284,16 @@ def sweep(g, synth, dev, stream):
     for B in synth.CONFIG4_BATCHES:
         x = synth.config4(B, device=dev)
         nb = kv_bytes(x)
+        bws = g.balanced_workspace(B, 32, 8, 128, dev)
+        out = torch.empty_like(x.q)
+        f = lambda: g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table,
+                                            x.context_lens, scale=x.scale, out=out, workspace=bws)
+        for _ in range(3):
+            f()
+        t = statistics.median(event_times(f, 20, stream))
+        print(json.dumps({"sweep": "long-context", "B": B, "T": 32768, "partition": "balanced",
+                          "us": round(t * 1e3, 2), "gbs": round(nb / (t * 1e-3) / 1e9, 1)}),
+              flush=True)
         for ns in synth.CONFIG4_SPLITS:
             ws = g.alloc_workspace(B, 32, 128, ns, dev) if ns > 1 else None
             out = torch.empty_like(x.q)
@@ -242,7 +310,17 @@ def sweep(g, synth, dev, stream):
         for B in synth.CONFIG5_BATCHES:
             x = synth.config5(B, hkv, device=dev)
             nb = kv_bytes(x)
-            best = None
+            bws = g.balanced_workspace(B, 32, hkv, 128, dev)
+            out = torch.empty_like(x.q)
+            f = lambda: g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table,
+                                                x.context_lens, scale=x.scale, out=out,
+                                                workspace=bws)
+            for _ in range(3):
+                f()
+            t = statistics.median(event_times(f, 20, stream))
+            print(json.dumps({"sweep": "batch-group", "B": B, "Hkv": hkv, "T": 1024,
+                              "partition": "balanced", "us": round(t * 1e3, 2),
+                              "gbs": round(nb / (t * 1e-3) / 1e9, 1)}), flush=True)
             for ns in (1, 2, 4, 8):
                 ws = g.alloc_workspace(B, 32, 128, ns, dev) if ns > 1 else None
                 out = torch.empty_like(x.q)

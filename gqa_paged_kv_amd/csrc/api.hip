@@ -17,7 +17,7 @@ int launch_gather(const void* cache, const int32_t* pt, const int32_t* lens, voi
 int launch_append(const void* src, const int32_t* pt, void* cache, int B, int S, int Hkv, int D,
                   int P, int max_pages, int elem_bytes, hipStream_t s);
 int launch_decode_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
-                           const int32_t* lens, void* out, void* ws, int B, int Hq, int Hkv,
+                           const int32_t* lens, void* out, void* slots, int B, int Hq, int Hkv,
                            int D, int max_pages, float scale, int dtype, hipStream_t s);
 int launch_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s);
@@ -53,14 +53,15 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
   if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
   if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
+  char* data = (char*)workspace;
   if (Hq / Hkv <= 8)
-    return gqa::launch_decode_balanced(q, k_cache, v_cache, page_table, context_lens, out,
-                                       workspace, B, Hq, Hkv, D, max_pages, scale, dtype, s);
+    return gqa::launch_decode_balanced(q, k_cache, v_cache, page_table, context_lens, out, data, B,
+                                       Hq, Hkv, D, max_pages, scale, dtype, s);
   const int ns = gqa_balanced_auto_splits(B, Hkv);
   if (ns == 1)
     return gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
                                     nullptr, B, Hq, Hkv, D, max_pages, 1, scale, dtype, s);
-  float* ws_o = (float*)workspace;
+  float* ws_o = (float*)data;
   float* ws_lse = ws_o + (size_t)B * Hq * ns * D;
   st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
                                 B, Hq, Hkv, D, max_pages, ns, scale, dtype, s);

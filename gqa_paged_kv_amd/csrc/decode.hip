@@ -350,9 +350,11 @@ static int launch_decode(const void* q, const void* k, const void* v, const int3
   float* wo = ns > 1 ? ws_o : nullptr;
   float* wl = ns > 1 ? ws_lse : nullptr;
   if constexpr (G <= 8) {
-    int kvw = 1;
-    while (kvw * 2 <= Hkv && kvw * 2 <= kRegsWaves) kvw *= 2;
-    const int groups = (Hkv + kvw - 1) / kvw;
+    // One KV head per workgroup: its 8 waves take the split's pages round-robin. (Grouping
+    // several KV heads per workgroup so that neighbouring (page, kv head) blocks are read
+    // together measured no faster, and leaves small batches with too few workgroups.)
+    const int kvw = 1;
+    const int groups = Hkv;
     hipLaunchKernelGGL((decode_regs_kernel<T, D, G>), dim3(groups * ns, B), dim3(kRegsThreads), 0,
                        stream, (const T*)q, (const T*)k, (const T*)v, pt, lens, (T*)out, wo, wl,
                        Hq, Hkv, max_pages, ns, kvw, scale * kLog2e);

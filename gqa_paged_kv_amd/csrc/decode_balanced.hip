@@ -10,26 +10,27 @@
 // "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
 // "核心参数调优：PackGQA与NumSplits的协同舞蹈") merged with the log-sum-exp rule.
 //
-// Three launches on the caller's stream:
-//   1. prefix_kernel   np_b = ceil(T_b / P) and its exclusive prefix sum over b;
-//   2. stream_kernel   persistent: wave w owns items [N w / W, N (w+1) / W) of the
-//                      b-major, then kv-head, then page ordered item list (N items).
-//                      A unit wholly inside one share is finished and written directly;
-//                      a cut unit leaves a partial (normalised output + natural-log LSE)
-//                      in the share's slot 0 (its first unit) or slot 1 (its last unit);
-//   3. fixup_kernel    merges the partials of every cut unit and zero-fills T_b = 0 rows.
-// Each wave keeps the next page in flight in VGPRs while computing the current one;
-// all G <= 8 heads of the group live in the wave, so a K/V row is read once.
+// Two launches on the caller's stream. Items are ordered b-major, then kv head, then
+// page; N items in all, wave w of nw owns [N w / nw, N (w+1) / nw).
+//   1. balanced_kernel (persistent): every wave computes N and finds the sequence holding
+//      its first item with wave-wide scans of ceil(T_b / P). A unit wholly inside one
+//      share is finished and written directly; a cut unit leaves, per piece, a partial
+//      (normalised output + natural-log LSE) in the share's slot 0 (its first unit) or
+//      slot 1 (its last unit). Each wave keeps two pages in flight in VGPRs while it
+//      computes a third; all G <= 8 heads of the group live in the wave, so a K/V row is
+//      read once.
+//   2. fixup_kernel: one wave per (sequence, KV head) unit merges the pieces of cut units
+//      and zero-fills the rows of sequences with T_b = 0. (Merging inside the first
+//      kernel would need device-scope fences that write back and invalidate the L2 on
+//      every piece: measured slower than this second launch.)
 #include "decode_common.h"
 
 namespace gqa {
 
 constexpr int kBalancedMaxWaves = 4096;  // upper bound of the persistent grid (workspace size)
 
-// Bytes of the workspace: [slots: waves x 2 x G x (D + 1) floats][prefix: B + 1 ints].
-static size_t balanced_slot_floats(int G, int D) { return (size_t)kBalancedMaxWaves * 2 * G * (D + 1); }
+// Workspace data region: kBalancedMaxWaves x 2 partial slots of G x (D + 1) floats.
 
-// ---- 1. page counts and their prefix sum (one workgroup of 256 threads) ---------------
 __device__ __forceinline__ int pages_of(const int32_t* __restrict__ context_lens, int b,
                                         int max_pages) {
   int T = context_lens[b];
@@ -37,94 +38,104 @@ __device__ __forceinline__ int pages_of(const int32_t* __restrict__ context_lens
   return (T + kPage - 1) / kPage;
 }
 
-__global__ __launch_bounds__(256) void prefix_kernel(const int32_t* __restrict__ context_lens,
-                                                     int32_t* __restrict__ prefix, int B,
-                                                     int max_pages) {
-  __shared__ int wave_tot[4];
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int per = (B + 255) / 256;  // consecutive sequences per thread
-  const int b0 = min(t * per, B), b1 = min(b0 + per, B);
-  int sum = 0;
-  for (int b = b0; b < b1; ++b) sum += pages_of(context_lens, b, max_pages);
-  int incl = sum;  // inclusive scan inside the wave
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) wave_tot[t >> 6] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < (t >> 6); ++w) base += wave_tot[w];
-  int run = base + incl - sum;  // exclusive prefix of this thread's first sequence
-  for (int b = b0; b < b1; ++b) {
-    prefix[b] = run;
-    run += pages_of(context_lens, b, max_pages);
-  }
-  if (t == 255) prefix[B] = run;
+__device__ __forceinline__ long wave_sum(long x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
 }
 
-// Largest b in [0, B) with Hkv * prefix[b] <= x, for 0 <= x < Hkv * prefix[B] (then
-// np_b > 0). 64-way search: every step samples 64 prefix entries, one per lane.
-__device__ __forceinline__ int find_sequence(const int32_t* __restrict__ prefix, int B, int Hkv,
-                                             long x, int lane) {
-  int lo = 0, hi = B;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int step = (hi - lo + 63) / 64;
-    const int idx = lo + lane * step;
-    const bool le = idx < hi && (long)Hkv * prefix[idx] <= x;
-    const int cnt = __popcll(__ballot(le));  // lanes 0 .. cnt-1 (lane 0 always)
-    const int nlo = lo + (cnt - 1) * step;
-    hi = min(hi, lo + cnt * step);
-    lo = nlo;
-  }
-  return lo;
+// share bounds and owner of an item (integer arithmetic shared by writers and mergers)
+__device__ __forceinline__ long share_lo(long N, int w, int nw) { return N * w / nw; }
+__device__ __forceinline__ int share_owner(long N, long x, int nw) {
+  return (int)(((x + 1) * nw - 1) / N);
 }
 
-// ---- 2. persistent streaming decode (G <= 8) --------------------------------------------
+// First sequence b whose items end past item x (so np_b > 0), with np_b and the index of
+// its first item: wave-wide inclusive scans of ceil(T_b / P), 64 sequences per step.
+__device__ __forceinline__ void locate_item(const int32_t* __restrict__ context_lens, int B,
+                                            int Hkv, int max_pages, long x, int lane, int& b,
+                                            int& np, long& seq_base) {
+  long base = 0;
+  for (int c = 0; c < B; c += kWave) {
+    const int n = c + lane < B ? pages_of(context_lens, c + lane, max_pages) : 0;
+    int incl = n;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    const unsigned long long hit = __ballot(base + (long)Hkv * incl > x);
+    if (hit) {
+      const int L = __ffsll((long long)hit) - 1;
+      b = c + L;
+      np = __shfl(n, L);
+      seq_base = base + (long)Hkv * (__shfl(incl, L) - np);
+      return;
+    }
+    base += (long)Hkv * __shfl(incl, kWave - 1);
+  }
+}
+
+// Index of the first item of sequence b (exclusive scan up to b).
+__device__ __forceinline__ long items_before(const int32_t* __restrict__ context_lens, int b,
+                                             int Hkv, int max_pages, int lane) {
+  long part = 0;
+  for (int bb = lane; bb < b; bb += kWave) part += pages_of(context_lens, bb, max_pages);
+  return (long)Hkv * wave_sum(part);
+}
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void stream_kernel(
+__global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ context_lens,
-    const int32_t* __restrict__ prefix, T* __restrict__ out, float* __restrict__ slots, int B,
-    int Hq, int Hkv, int max_pages, float scale_log2) {
+    T* __restrict__ out, float* __restrict__ slots, int B, int Hq, int Hkv, int max_pages,
+    float scale_log2) {
   using S = DecodeShape<T, D, G>;
   static_assert(S::HG == 1, "all heads of the group in one wave");
   constexpr int W32 = S::W32;
   constexpr int E = S::E;
+  constexpr int SLOT = G * (D + 1);
 
   const int lane = lane_id();
   const int r = lane >> 4;
   const int qd = lane & 15;
   const int nw = gridDim.x * kDecodeWaves;
   const int gw = blockIdx.x * kDecodeWaves + wave_id();
-  const long N = (long)Hkv * prefix[B];
-  const long lo = N * gw / nw;
-  const long hi = N * (gw + 1) / nw;
+
+  // ---- total item count N = Hkv * sum_b ceil(T_b / P) ----
+  long part = 0;
+  for (int bb = lane; bb < B; bb += kWave) part += pages_of(context_lens, bb, max_pages);
+  const long N = (long)Hkv * wave_sum(part);
+
+  if (N == 0) return;
+  const long lo = share_lo(N, gw, nw);
+  const long hi = share_lo(N, gw + 1, nw);
   if (lo >= hi) return;
 
-  // cursor over items: sequence b, kv head kvh, page pg of np pages
-  int b = find_sequence(prefix, B, Hkv, lo, lane);
-  int np = prefix[b + 1] - prefix[b];
-  long rem = lo - (long)Hkv * prefix[b];
+  // ---- locate the sequence holding item lo ----
+  int b = 0, np = 1;
+  long seq_base = 0;  // first item of sequence b
+  locate_item(context_lens, B, Hkv, max_pages, lo, lane, b, np, seq_base);
+  const long rem = lo - seq_base;
   int kvh = (int)(rem / np);
   int pg = (int)(rem % np);
   const size_t page_stride = (size_t)Hkv * S::PAGE;
 
+  // move a cursor to the next item (skipping empty sequences)
   auto advance = [&](int& cb, int& ckv, int& cpg, int& cnp) {
     if (++cpg == cnp) {
       cpg = 0;
       if (++ckv == Hkv) {
         ckv = 0;
+        int n = 0;
         do {
           ++cb;
-        } while (cb < B && prefix[cb + 1] == prefix[cb]);
-        cnp = cb < B ? prefix[cb + 1] - prefix[cb] : 1;
+          n = cb < B ? pages_of(context_lens, cb, max_pages) : 1;
+        } while (n == 0);
+        cnp = n;
       }
     }
   };
 
-  uint32_t kb[2][4][W32], vb[2][4][W32];
+  uint32_t kb[3][4][W32], vb[3][4][W32];
   auto load_page = [&](int buf, int cb, int ckv, int cpg) {
     const size_t off = (size_t)page_table[(size_t)cb * max_pages + cpg] * page_stride +
                        (size_t)ckv * S::PAGE + r * S::ROW;
@@ -139,48 +150,49 @@ __global__ __launch_bounds__(kDecodeThreads) void stream_kernel(
 
   WaveState<T, D, G> st;
   long seg_start = lo;  // first item of the current segment
-  int seg_pg0 = pg;     // its page within the unit
   st.init(q + ((size_t)b * Hq + kvh * G) * D, qd);
   int T_b = min(context_lens[b], max_pages * kPage);
 
-  // Finish the segment that ends at the current item: merge rows, then write the final
-  // output (the whole unit is in this share) or a partial into slot 0 / 1.
-  auto finish = [&](bool whole_unit) {
-    st.merge_rows();
-    if (whole_unit) {
+  auto store_row = [&](T* dst, int hw, float inv) {
+    if (r == 0) {
 #pragma unroll
-      for (int hw = 0; hw < G; ++hw) {
-        const float inv = 1.0f / st.l[hw];
-        T* dst = out + ((size_t)b * Hq + kvh * G + hw) * D;
-        if (r == 0) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float o = st.acc[hw][e] * inv;
-            if constexpr (sizeof(T) == 2) {
-              ((uint16_t*)dst)[lane_dim<T, D>(qd, e)] = f32_to_bf16(o);
-            } else {
-              dst[lane_dim<T, D>(qd, e)] = o;
-            }
-          }
+      for (int e = 0; e < E; ++e) {
+        const float o = st.acc[hw][e] * inv;
+        if constexpr (sizeof(T) == 2) {
+          ((uint16_t*)dst)[lane_dim<T, D>(qd, e)] = f32_to_bf16(o);
+        } else {
+          dst[lane_dim<T, D>(qd, e)] = o;
         }
-      }
-    } else {
-      const int slot = seg_start == lo ? 0 : 1;
-      float* base = slots + ((size_t)gw * 2 + slot) * G * (D + 1);
-#pragma unroll
-      for (int hw = 0; hw < G; ++hw) {
-        const float inv = 1.0f / st.l[hw];
-        if (r == 0) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) base[hw * (D + 1) + lane_dim<T, D>(qd, e)] = st.acc[hw][e] * inv;
-        }
-        if (lane == 0) base[hw * (D + 1) + D] = (st.m[hw] + __builtin_log2f(st.l[hw])) * kLn2;
       }
     }
   };
 
-  // Consume item i (the current cursor) from buffer `buf`, then open the next segment if
-  // the next item starts a new unit.
+  // Finish the segment that ends at item i: merge the 4 DPP rows, then write the output
+  // (the whole unit is in this share) or the piece's partial.
+  auto finish = [&](long i) {
+    st.merge_rows();
+    const long first = i - pg;  // first item of the unit (pg = page of item i)
+    if (seg_start == first && pg + 1 == np) {
+#pragma unroll
+      for (int hw = 0; hw < G; ++hw)
+        store_row(out + ((size_t)b * Hq + kvh * G + hw) * D, hw, 1.0f / st.l[hw]);
+      return;
+    }
+    const int slot = seg_start == lo ? 0 : 1;
+    float* base = slots + ((size_t)gw * 2 + slot) * SLOT;
+#pragma unroll
+    for (int hw = 0; hw < G; ++hw) {
+      const float inv = 1.0f / st.l[hw];
+      if (r == 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) base[hw * (D + 1) + lane_dim<T, D>(qd, e)] = st.acc[hw][e] * inv;
+      }
+      if (lane == 0) base[hw * (D + 1) + D] = (st.m[hw] + __builtin_log2f(st.l[hw])) * kLn2;
+    }
+  };
+
+  // Consume item i from buffer `buf`, then move the compute cursor; open a new segment
+  // when the next item starts a new unit.
   auto consume = [&](int buf, long i) {
     const int tok0 = pg * kPage + r;
     if (pg + 1 < np) {
@@ -189,127 +201,139 @@ __global__ __launch_bounds__(kDecodeThreads) void stream_kernel(
       st.template page<true>(kb[buf], vb[buf], tok0, T_b, scale_log2);
     }
     const bool unit_end = pg + 1 == np;
-    if (unit_end || i + 1 == hi) {
-      finish(unit_end && seg_pg0 == 0);
-    }
+    if (unit_end || i + 1 == hi) finish(i);
     advance(b, kvh, pg, np);
     if (unit_end && i + 1 < hi) {
       seg_start = i + 1;
-      seg_pg0 = 0;
-      st.reset();
       st.init(q + ((size_t)b * Hq + kvh * G) * D, qd);
       T_b = min(context_lens[b], max_pages * kPage);
     }
   };
 
-  // The load cursor runs one item ahead of the compute cursor. The prefetch is issued on
-  // every step (past the share's end it re-reads the current page, an L2 hit) so that the
-  // number of loads in flight is the same on every path and the wait before each page is
-  // exactly "all but the newest page".
+  // The load cursor runs two items ahead of the compute cursor (three page buffers). The
+  // prefetch is issued on every step (past the share's end it re-reads the current page,
+  // an L2 hit) so that the loads in flight are the same on every path and the wait before
+  // each page is exactly "all but the two newest pages".
   int lb = b, lkv = kvh, lpg = pg, lnp = np;
   load_page(0, lb, lkv, lpg);
-  for (long i = lo; i < hi; i += 2) {
-    if (i + 1 < hi) advance(lb, lkv, lpg, lnp);
-    load_page(1, lb, lkv, lpg);
+  if (lo + 1 < hi) advance(lb, lkv, lpg, lnp);
+  load_page(1, lb, lkv, lpg);
+  for (long i = lo; i < hi; i += 3) {
+    if (i + 2 < hi) advance(lb, lkv, lpg, lnp);
+    load_page(2, lb, lkv, lpg);
     consume(0, i);
     if (i + 1 >= hi) break;
-    if (i + 2 < hi) advance(lb, lkv, lpg, lnp);
+    if (i + 3 < hi) advance(lb, lkv, lpg, lnp);
     load_page(0, lb, lkv, lpg);
     consume(1, i + 1);
+    if (i + 2 >= hi) break;
+    if (i + 4 < hi) advance(lb, lkv, lpg, lnp);
+    load_page(1, lb, lkv, lpg);
+    consume(2, i + 2);
   }
 }
 
-// ---- 3. merge the partials of cut units; zero rows of empty sequences --------------------
-// One workgroup per (sequence, KV head) unit. The pieces' LSEs are read once, in parallel,
-// into LDS and turned into normalised weights; each output then sums independent loads.
-constexpr int kFixupThreads = 256;
-constexpr int kFixupMaxParts = 512;  // pieces merged per LDS pass
+// ---- fix-up: merge the pieces of cut units; zero rows of empty sequences ----------------
+// One wave per (sequence, KV head) unit. Lane p holds piece p's LSEs (all heads); the
+// weights come from wave reductions; each lane then sums its D / 64 dims over the pieces
+// with the loads of four pieces in flight at a time. Pieces are taken 64 at a time.
+constexpr int kFixupWaves = 4;
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kFixupThreads) void fixup_kernel(const float* __restrict__ slots,
-                                                             const int32_t* __restrict__ prefix,
-                                                             T* __restrict__ out, int B, int Hq,
-                                                             int Hkv, int nw) {
-  __shared__ float wgt[kFixupMaxParts * G];
-  __shared__ int part_off[kFixupMaxParts];  // float offset of each piece's slot
-  __shared__ float red_m[G], red_l[G];
-  const int u = blockIdx.x;
-  const int b = u / Hkv;
-  const int kvh = u % Hkv;
-  const int np = prefix[b + 1] - prefix[b];
-  const long N = (long)Hkv * prefix[B];
+__global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
+    const float* __restrict__ slots, const int32_t* __restrict__ context_lens,
+    T* __restrict__ out, int B, int Hq, int Hkv, int max_pages, int nw) {
+  constexpr int SLOT = G * (D + 1);
+  constexpr int DL = D / kWave;  // dims per lane
+  const int lane = lane_id();
+  const long u = (long)blockIdx.x * kFixupWaves + wave_id();
+  if (u >= (long)B * Hkv) return;
+  const int b = (int)(u / Hkv);
+  const int kvh = (int)(u % Hkv);
+  // N and the first item of sequence b in one pass over the page counts
+  long part_all = 0, part_before = 0;
+  for (int bb = lane; bb < B; bb += kWave) {
+    const int n = pages_of(context_lens, bb, max_pages);
+    part_all += n;
+    part_before += bb < b ? n : 0;
+  }
+  const long N = (long)Hkv * wave_sum(part_all);
+  const int np = pages_of(context_lens, b, max_pages);
   T* dst = out + ((size_t)b * Hq + kvh * G) * D;
   if (np == 0) {  // T_b == 0: the output is zero
-    for (int i = threadIdx.x; i < G * D; i += kFixupThreads) {
+    for (int i = lane; i < G * D; i += kWave) {
       if constexpr (sizeof(T) == 2) ((uint16_t*)dst)[i] = 0; else dst[i] = 0.f;
     }
     return;
   }
-  const long first = (long)Hkv * prefix[b] + (long)kvh * np;
-  const long last = first + np - 1;
-  // wave w owns [N w / nw, N (w+1) / nw): the owner of item x is floor(((x+1) nw - 1) / N)
-  const int w0 = (int)(((first + 1) * nw - 1) / N);
-  const int w1 = (int)(((last + 1) * nw - 1) / N);
+  const long first = (long)Hkv * wave_sum(part_before) + (long)kvh * np;
+  const int w0 = share_owner(N, first, nw);
+  const int w1 = share_owner(N, first + np - 1, nw);
   if (w0 == w1) return;  // finished and written by its wave
-  const bool head_is_first = (N * w0 / nw) == first;
+  const bool head_is_first = share_lo(N, w0, nw) == first;
 
-  float acc[(G * D + kFixupThreads - 1) / kFixupThreads];
-  for (int k = 0; k < (G * D + kFixupThreads - 1) / kFixupThreads; ++k) acc[k] = 0.f;
-  float m_run[G], l_run[G];  // running max / sum per head (same in every thread)
-  for (int hl = 0; hl < G; ++hl) { m_run[hl] = -INFINITY; l_run[hl] = 0.f; }
-
-  for (int c0 = w0; c0 <= w1; c0 += kFixupMaxParts) {
-    const int nparts = min(kFixupMaxParts, w1 - c0 + 1);
-    // piece p = wave c0 + p; empty shares (fewer items than waves) wrote nothing
-    for (int i = threadIdx.x; i < nparts * G; i += kFixupThreads) {
-      const int p = i / G, hl = i % G;
-      const int w = c0 + p;
-      const int slot = (w == w0 && !head_is_first) ? 1 : 0;
-      const size_t off = (((size_t)w * 2 + slot) * G + hl) * (D + 1);
-      const bool empty = N * w / nw == N * (w + 1) / nw;
-      wgt[i] = empty ? -INFINITY : slots[off + D];
-      if (hl == 0) part_off[p] = (int)(((size_t)w * 2 + slot) * G * (D + 1));
-    }
-    __syncthreads();
-    if (threadIdx.x < G) {
-      const int hl = threadIdx.x;
-      float M = m_run[hl];
-      for (int p = 0; p < nparts; ++p) M = fmaxf(M, wgt[p * G + hl]);
-      red_m[hl] = M;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nparts * G; i += kFixupThreads) {
-      const float lse = wgt[i];
-      wgt[i] = lse == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lse - red_m[i % G]) * kLog2e);
-    }
-    __syncthreads();
-    for (int k = 0; k * kFixupThreads + (int)threadIdx.x < G * D; ++k) {
-      const int idx = k * kFixupThreads + threadIdx.x;
-      const int hl = idx / D, d = idx % D;
-      const float scale_old = m_run[hl] == -INFINITY ? 0.f
-                              : __builtin_amdgcn_exp2f((m_run[hl] - red_m[hl]) * kLog2e);
-      float a = acc[k] * scale_old;
-#pragma unroll 4
-      for (int p = 0; p < nparts; ++p) {
-        const float wv = wgt[p * G + hl];  // 0 for an empty share: its slot was never written
-        if (wv != 0.f) a = fmaf(wv, slots[part_off[p] + hl * (D + 1) + d], a);
-      }
-      acc[k] = a;
-    }
-    for (int hl = 0; hl < G; ++hl) {
-      const float scale_old = m_run[hl] == -INFINITY ? 0.f
-                              : __builtin_amdgcn_exp2f((m_run[hl] - red_m[hl]) * kLog2e);
-      float l = l_run[hl] * scale_old;
-      for (int p = 0; p < nparts; ++p) l += wgt[p * G + hl];
-      l_run[hl] = l;
-      m_run[hl] = red_m[hl];
-    }
-    __syncthreads();
+  float m_run[G], den[G], num[G][DL];
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl) {
+    m_run[hl] = -INFINITY;
+    den[hl] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DL; ++j) num[hl][j] = 0.f;
   }
-  for (int k = 0; k * kFixupThreads + (int)threadIdx.x < G * D; ++k) {
-    const int idx = k * kFixupThreads + threadIdx.x;
-    const float o = acc[k] / l_run[idx / D];
-    if constexpr (sizeof(T) == 2) ((uint16_t*)dst)[idx] = f32_to_bf16(o); else dst[idx] = o;
+  for (int c0 = w0; c0 <= w1; c0 += kWave) {
+    const int np_c = min(kWave, w1 - c0 + 1);
+    // lane p: piece c0 + p (empty shares wrote nothing: weight 0, slot never read)
+    const int w = c0 + lane;
+    const bool live = lane < np_c && share_lo(N, w, nw) != share_lo(N, w + 1, nw);
+    const int slot = (w == w0 && !head_is_first) ? 1 : 0;
+    const int off = live ? (int)(((size_t)w * 2 + slot) * SLOT) : 0;
+    float lse[G];
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl) lse[hl] = live ? slots[off + hl * (D + 1) + D] : -INFINITY;
+    float wgt[G];
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl) {
+      float M = lse[hl];
+      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      M = fmaxf(M, m_run[hl]);
+      const float rescale = m_run[hl] == -INFINITY ? 0.f
+                            : __builtin_amdgcn_exp2f((m_run[hl] - M) * kLog2e);
+      wgt[hl] = live ? __builtin_amdgcn_exp2f((lse[hl] - M) * kLog2e) : 0.f;
+      den[hl] *= rescale;
+      float ws = wgt[hl];
+      for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+      den[hl] += ws;
+#pragma unroll
+      for (int j = 0; j < DL; ++j) num[hl][j] *= rescale;
+      m_run[hl] = M;
+    }
+    for (int p0 = 0; p0 < np_c; p0 += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int p = p0 + k;  // wave-uniform
+        const int po = __shfl(off, p);
+        const bool pl = p < np_c && __shfl((int)live, p) != 0;
+        if (!pl) continue;
+#pragma unroll
+        for (int hl = 0; hl < G; ++hl) {
+          const float wv = __shfl(wgt[hl], p);
+#pragma unroll
+          for (int j = 0; j < DL; ++j)
+            num[hl][j] = fmaf(wv, slots[po + hl * (D + 1) + lane + kWave * j], num[hl][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl) {
+    const float inv = 1.0f / den[hl];
+#pragma unroll
+    for (int j = 0; j < DL; ++j) {
+      const float o = num[hl][j] * inv;
+      const int d = lane + kWave * j;
+      if constexpr (sizeof(T) == 2) ((uint16_t*)(dst + hl * D))[d] = f32_to_bf16(o);
+      else dst[hl * D + d] = o;
+    }
   }
 }
 
@@ -317,9 +341,11 @@ __global__ __launch_bounds__(kFixupThreads) void fixup_kernel(const float* __res
 
 template <typename T, int D, int G>
 static int launch_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
-                           const int32_t* lens, void* out, void* workspace, int B, int Hq,
+                           const int32_t* lens, void* out, void* slots_ws, int B, int Hq,
                            int Hkv, int max_pages, float scale, hipStream_t s) {
-  static int grid_cache[64] = {0};  // persistent grid per device (resident workgroups)
+  // Persistent grid = resident workgroups; a per-device cache of an occupancy query
+  // (every thread computes and stores the same value).
+  static int grid_cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GQA_ERR_LAUNCH;
   int grid = grid_cache[dev];
@@ -327,21 +353,20 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return GQA_ERR_LAUNCH;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<T, D, G>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel<T, D, G>,
                                                      kDecodeThreads, 0) != hipSuccess)
       return GQA_ERR_LAUNCH;
     grid = cus * (per_cu > 0 ? per_cu : 1);
     if (grid * kDecodeWaves > kBalancedMaxWaves) grid = kBalancedMaxWaves / kDecodeWaves;
     grid_cache[dev] = grid;
   }
-  float* slots = (float*)workspace;
-  int32_t* prefix = (int32_t*)(slots + balanced_slot_floats(G, D));
-  hipLaunchKernelGGL(prefix_kernel, dim3(1), dim3(256), 0, s, lens, prefix, B, max_pages);
-  hipLaunchKernelGGL((stream_kernel<T, D, G>), dim3(grid), dim3(kDecodeThreads), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, pt, lens, prefix, (T*)out, slots, B,
-                     Hq, Hkv, max_pages, scale * kLog2e);
-  hipLaunchKernelGGL((fixup_kernel<T, D, G>), dim3((unsigned)(B * Hkv)), dim3(kFixupThreads), 0, s,
-                     slots, prefix, (T*)out, B, Hq, Hkv, grid * kDecodeWaves);
+  float* slots = (float*)slots_ws;
+  hipLaunchKernelGGL((balanced_kernel<T, D, G>), dim3(grid), dim3(kDecodeThreads), 0, s,
+                     (const T*)q, (const T*)k, (const T*)v, pt, lens, (T*)out, slots, B, Hq, Hkv,
+                     max_pages, scale * kLog2e);
+  const unsigned fix_grid = (unsigned)(((long)B * Hkv + kFixupWaves - 1) / kFixupWaves);
+  hipLaunchKernelGGL((fixup_kernel<T, D, G>), dim3(fix_grid), dim3(kFixupWaves * kWave), 0, s,
+                     slots, lens, (T*)out, B, Hq, Hkv, max_pages, grid * kDecodeWaves);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
@@ -356,11 +381,6 @@ static int balanced_group(int G, const void* q, const void* k, const void* v, co
     case 8: return launch_balanced<T, D, 8>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
     default: return GQA_ERR_UNSUPPORTED;
   }
-}
-
-size_t balanced_workspace_bytes(int B, int Hq, int Hkv, int D) {
-  const int G = Hq / Hkv;
-  return balanced_slot_floats(G, D) * sizeof(float) + (size_t)(B + 1) * sizeof(int32_t);
 }
 
 int launch_decode_balanced(const void* q, const void* k, const void* v, const int32_t* pt,

@@ -84,13 +84,15 @@ int gqa_balanced_auto_splits(int B, int Hkv) {
   return (int)(ns < 1 ? 1 : (ns > 16 ? 16 : ns));
 }
 
+// Workspace of the balanced entry point: per-wave partial slots (G <= 8) or the split
+// partials (G >= 16).
 size_t gqa_decode_balanced_workspace_bytes(int B, int Hq, int Hkv, int D) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
   const size_t G = (size_t)(Hq / Hkv);
-  // persistent path: 4096 waves x 2 slots x G x (D + 1) floats, then B + 1 ints
-  const size_t stream_bytes = (size_t)4096 * 2 * G * (D + 1) * sizeof(float) + (size_t)(B + 1) * 4;
+  // persistent path: 4096 waves x 2 slots x G x (D + 1) floats
+  const size_t slot_bytes = (size_t)4096 * 2 * G * (D + 1) * sizeof(float);
   const size_t split_bytes = gqa_decode_workspace_bytes(B, Hq, D, gqa_balanced_auto_splits(B, Hkv));
-  return stream_bytes > split_bytes ? stream_bytes : split_bytes;
+  return slot_bytes > split_bytes ? slot_bytes : split_bytes;
 }
 
 int gqa_validate_prefill(const void* q, const void* k, const void* v, const void* k_cache,

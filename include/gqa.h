@@ -101,10 +101,10 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *
  *   workspace        device scratch of at least
  *                    gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D) bytes, 256-byte
- *                    aligned, owned by the caller; contents need no initialisation and
- *                    are overwritten. Calls that share a workspace must not overlap.
+ *                    aligned, owned by the caller; no initialisation needed, contents are
+ *                    overwritten. Calls that share a workspace must not overlap in time.
  *   other arguments  as for gqa_decode_paged.
- * Enqueues three kernels (page-count prefix sum, decode, fix-up) on `stream`.
+ * Enqueues two kernels on `stream` (decode + fix-up; for G >= 16 split decode + combine).
  */
 int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* page_table, const int32_t* context_lens, void* out,
