@@ -258,7 +258,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_causal_bf16_B4_S2048_Hq32_Hkv8"),
-                         "kernel": "append_kernel x2 + prefill_causal_kernel<4> (one call)"},
+                         "kernel": "prefill_causal_kernel<4> (attention + KV append, one launch)"},
             "flops_per_call": fl,
         }
         del p, pout

@@ -14,12 +14,11 @@ int launch_combine(const float* ws_o, const float* ws_lse, void* out, int B, int
                    int ns, int dtype, hipStream_t s);
 int launch_gather(const void* cache, const int32_t* pt, const int32_t* lens, void* dst, int B,
                   int Hkv, int D, int P, int max_pages, int dtype, hipStream_t s);
-int launch_append(const void* src, const int32_t* pt, void* cache, int B, int S, int Hkv, int D,
-                  int P, int max_pages, int elem_bytes, hipStream_t s);
 int launch_decode_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
                            const int32_t* lens, void* out, void* slots, int B, int Hq, int Hkv,
                            int D, int max_pages, float scale, int dtype, hipStream_t s);
-int launch_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
+int launch_prefill(const void* q, const void* k, const void* v, void* out, void* k_cache,
+                   void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s);
 }  // namespace gqa
 
@@ -84,12 +83,9 @@ int gqa_prefill_causal(const void* q, const void* k, const void* v, void* k_cach
   int st = gqa_validate_prefill(q, k, v, k_cache, v_cache, page_table, out, B, S, Hq, Hkv, D, P,
                                 max_pages, num_pages, scale, dtype);
   if (st != GQA_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  st = gqa::launch_append(k, page_table, k_cache, B, S, Hkv, D, P, max_pages, 2, s);
-  if (st != GQA_OK) return st;
-  st = gqa::launch_append(v, page_table, v_cache, B, S, Hkv, D, P, max_pages, 2, s);
-  if (st != GQA_OK) return st;
-  return gqa::launch_prefill(q, k, v, out, B, S, Hq, Hkv, D, scale, s);
+  // one kernel: attention plus the append of the new K/V rows into the cache
+  return gqa::launch_prefill(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv,
+                             D, scale, (hipStream_t)stream);
 }
 
 int gqa_gather_paged(const void* cache, const int32_t* page_table, const int32_t* context_lens,

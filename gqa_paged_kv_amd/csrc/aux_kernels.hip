@@ -1,9 +1,9 @@
-// Split combine, KV append and the test-only gather (gfx950).
+// Split combine and the test-only gather (gfx950).
 //
 // combine: merges NumSplits partials (page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践",
 //   section "核心参数调优：PackGQA与NumSplits的协同舞蹈") with the log-sum-exp rule:
 //   out = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M), M = max_s lse_s.
-// append / gather: bit-exact copies between token-major K/V and the paged pool,
+// gather: bit-exact copy from the paged pool to token-major K/V,
 //   token t of sequence b <-> slot t % P of page page_table[b][t / P] (page
 //   "TensorRT对Grouped Query Attention的支持进展", section "动态形状与KV Cache管理";
 //   page "TensorRT-LLM与TensorRT核心差异解析", section 4.2.2).
@@ -71,28 +71,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ ca
   }
 }
 
-// Write new[b][t][kvh][:] (t < S) into slot t % P of page page_table[b][t / P].
-__global__ __launch_bounds__(256) void append_kernel(const char* __restrict__ src,
-                                                     const int32_t* __restrict__ page_table,
-                                                     char* __restrict__ cache, int S, int Hkv,
-                                                     int row_bytes, int P, int max_pages) {
-  const int lp = blockIdx.x;
-  const int b = blockIdx.y;
-  const int phys = page_table[(size_t)b * max_pages + lp];
-  const int chunks_row = row_bytes / 16;
-  const int chunks = Hkv * P * chunks_row;
-  for (int idx = threadIdx.x; idx < chunks; idx += blockDim.x) {
-    const int kvh = idx / (P * chunks_row);
-    const int rem = idx % (P * chunks_row);
-    const int slot = rem / chunks_row;
-    const int c = rem % chunks_row;
-    const int t = lp * P + slot;
-    if (t >= S) continue;
-    const u32x4_t v = *(const u32x4_t*)(src + (((size_t)b * S + t) * Hkv + kvh) * row_bytes + c * 16);
-    *(u32x4_t*)(cache + (((size_t)phys * Hkv + kvh) * P + slot) * row_bytes + c * 16) = v;
-  }
-}
-
 int launch_combine(const float* ws_o, const float* ws_lse, void* out, int B, int Hq, int D,
                    int ns, int dtype, hipStream_t s) {
   dim3 grid((unsigned)B * Hq);
@@ -114,12 +92,5 @@ int launch_gather(const void* cache, const int32_t* pt, const int32_t* lens, voi
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
-int launch_append(const void* src, const int32_t* pt, void* cache, int B, int S, int Hkv, int D,
-                  int P, int max_pages, int elem_bytes, hipStream_t s) {
-  const int n_pages = (S + P - 1) / P;
-  hipLaunchKernelGGL(append_kernel, dim3(n_pages, B), dim3(256), 0, s, (const char*)src, pt,
-                     (char*)cache, S, Hkv, D * elem_bytes, P, max_pages);
-  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
-}
 
 }  // namespace gqa

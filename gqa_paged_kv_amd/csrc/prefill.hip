@@ -25,6 +25,8 @@
 //   O^T += V^T P^T 16 MFMAs; A = V^T read straight from the key-major V tile with
 //                 ds_read_b64_tr_b16 (no transpose pass), B = P^T from registers (bf16).
 // K/V tiles stream HBM -> LDS with global_load_lds_dwordx4, double-buffered.
+#include <type_traits>
+
 #include "device_common.h"
 #include "../../include/gqa.h"
 
@@ -39,19 +41,40 @@ constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * kWave;
 constexpr int ROWB = D * 2;     // bytes per K/V row
 constexpr int TILE = BN * ROWB; // 16 KiB
-constexpr int LOADS = 2 * TILE / (16 * THREADS);  // DMA loads per thread per tile (4)
 constexpr float kLazy = 8.0f;   // log2 growth tolerated before rescaling O
 
 // Row swizzles (16-byte chunk index XOR): K rows are read 16 at a time at one chunk,
 // V rows 4 at a time over 4 chunks (transpose reads).
 __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+
+// 16 bytes per lane from a raw buffer straight into LDS (buffer_load_dwordx4 ... lds; LDS
+// address M0 + 16 * lane). Written as assembly so that the compiler does not track it: it
+// would otherwise treat every later transpose read of LDS as possibly depending on it and
+// wait for all loads in flight. The kernel orders the LDS write itself (s_waitcnt vmcnt on
+// the issuing wave, then a workgroup barrier) before any wave reads that stage.
+__device__ __forceinline__ void buffer_dma16(u32x4_t rsrc, uint32_t voffset, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
+// Raw buffer descriptor: 48-bit base, stride 0, num_records bytes, gfx9 data format word.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)num_records), 0x00020000u};
+}
 }  // namespace prefill
 
 template <int G>
-__global__ __launch_bounds__(prefill::THREADS) void prefill_causal_kernel(
+__global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_causal_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    bf16_t* __restrict__ out, int S, int Hq, int Hkv, float scale_log2, int n_qtiles) {
+    bf16_t* __restrict__ out, bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ page_table, int max_pages, int S, int Hq, int Hkv,
+    float scale_log2, int n_qtiles) {
   using namespace prefill;
   constexpr int BMPOS = 256 / G;  // positions per q-tile
   constexpr int PB = 8 / G;       // 32-position blocks per head
@@ -75,11 +98,20 @@ __global__ __launch_bounds__(prefill::THREADS) void prefill_causal_kernel(
   const int wave_tiles = qa < S ? (min(qa + 31, S - 1)) / BN + 1 : 0;
   const int wg_tiles = (min(q0 + BMPOS, S) - 1) / BN + 1;
 
-  const size_t kv_row_stride = (size_t)Hkv * D;  // elements between consecutive tokens
-  const bf16_t* k_base = k + (size_t)b * S * kv_row_stride + (size_t)kvh * D;
-  const bf16_t* v_base = v + (size_t)b * S * kv_row_stride + (size_t)kvh * D;
+  // K and V of (b, kvh) as raw buffers; token t's row starts at byte t * row_stride.
+  const uint32_t row_stride = (uint32_t)Hkv * ROWB;
+  const size_t bkv_off = (size_t)b * S * Hkv * D + (size_t)kvh * D;
+  const uint32_t extent = (uint32_t)(S - 1) * row_stride + ROWB;
+  const u32x4_t k_rsrc = make_rsrc(k + bkv_off, extent);
+  const u32x4_t v_rsrc = make_rsrc(v + bkv_off, extent);
 
-  // Q^T operand: lane holds dims 16s + 8*half .. +7 of query my_q, for s = 0..7.
+  // Q^T operand: lane holds dims 16s + 8*half .. +7 of query my_q, for s = 0..7. The
+  // softmax below takes the row max of the raw scores and applies the scale inside the
+  // exponent, which needs scale > 0: a negative scale is moved onto Q (sign flip, exact),
+  // and a zero scale is raised to 1e-30 so that masked (-inf) scores still give exp2 = 0
+  // (every finite score then maps to exp2(~0) = 1 in fp32, the uniform weights of scale 0).
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float sl2 = fmaxf(fabsf(scale_log2), 1e-30f);
   u32x4_t qop[8];
   {
     const bool ok = my_q < S;
@@ -87,7 +119,7 @@ __global__ __launch_bounds__(prefill::THREADS) void prefill_causal_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4_t t = *(const u32x4_t*)(qrow + 16 * s + 8 * half);
-      qop[s] = ok ? t : u32x4_t{0u, 0u, 0u, 0u};
+      qop[s] = ok ? (t ^ qsign) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
 
@@ -97,64 +129,121 @@ __global__ __launch_bounds__(prefill::THREADS) void prefill_causal_kernel(
   float m_run = -INFINITY;
   float l_half = 0.f;
 
-  auto issue_tile = [&](int kt, int st) {
+  // DMA plan of one tile: wave-instruction wi = ii * WAVES + w moves rows 4*(wi%16) ..
+  // +3 of K (ii = 0, 1) or V (ii = 2, 3), 16 lanes per row. A lane's byte offset in the
+  // buffer is fixed up to the tile base; rows past S - 1 are clamped onto row S - 1.
+  static_assert(WAVES * 2 == 16, "two loads move a K tile, two a V tile");
+  const uint32_t smem0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&smem[0][0][0];
+  uint32_t dma_off[4], dma_last[4];
 #pragma unroll
-    for (int ii = 0; ii < LOADS; ++ii) {
-      const int wi = ii * WAVES + w;   // wave instruction index: 0..15 K, 16..31 V
-      const bool is_v = wi >= 16;
-      const int row = 4 * (wi & 15) + (lane >> 4);
-      const int chunk = (lane & 15) ^ (is_v ? v_swz(row) : k_swz(row));
-      const int key = min(kt * BN + row, S - 1);
-      const bf16_t* src = (is_v ? v_base : k_base) + (size_t)key * kv_row_stride + chunk * 8;
-      lds_dma16(src, &smem[st][is_v ? 1 : 0][(wi & 15) * 1024]);
+  for (int ii = 0; ii < 4; ++ii) {
+    const int r = 4 * ((ii & 1) * WAVES + w) + (lane >> 4);
+    const int chunk = (lane & 15) ^ (ii >= 2 ? v_swz(r) : k_swz(r));
+    dma_off[ii] = (uint32_t)r * row_stride + chunk * 16;
+    dma_last[ii] = (uint32_t)(S - 1) * row_stride + chunk * 16;
+  }
+  const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(smem0 + w * 1024);
+  auto issue_k = [&](int t, int st) {  // K tile t into stage st
+    const uint32_t off = (uint32_t)t * BN * row_stride;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+      buffer_dma16(k_rsrc, min(dma_off[ii] + off, dma_last[ii]),
+                   dma_lds + st * 2 * TILE + ii * WAVES * 1024);
+  };
+  auto issue_v = [&](int t, int st) {  // V tile t into stage st
+    const uint32_t off = (uint32_t)t * BN * row_stride;
+#pragma unroll
+    for (int ii = 2; ii < 4; ++ii)
+      buffer_dma16(v_rsrc, min(dma_off[ii] + off, dma_last[ii]),
+                   dma_lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
+  };
+
+  // Per-lane LDS byte offsets, fixed for the whole kernel (stage, key block and row step
+  // are compile-time and become instruction offsets):
+  //   K, A operand of step s: row l32, 16-byte chunk (2s + half) ^ (l32 % 16);
+  //   V^T, transpose reads: lane (g16, i16) reads row 4*(g16/2) + i16/4 (+16 sp + 8 r) at
+  //   chunk 4*mbd + 2*(g16%2) + (i16%4)/2 with the row swizzle 4*(row % 4), i.e.
+  //   4*(mbd ^ (i16/4)) + ..., byte (i16%2)*8 of the chunk.
+  uint32_t koff[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = smem0 + l32 * ROWB + (((2 * s + half) ^ (l32 & 15)) << 4);
+  const int g16 = lane >> 4;
+  const int i16 = lane & 15;
+  const uint32_t vlane = smem0 + TILE + (4 * (g16 >> 1) + (i16 >> 2)) * ROWB +
+                         (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 + (i16 & 1) * 8;
+  uint32_t voff[4];
+#pragma unroll
+  for (int mbd = 0; mbd < 4; ++mbd) voff[mbd] = vlane + ((mbd ^ (i16 >> 2)) << 6);
+
+  // S^T = K Q^T for the tile in stage ST: two 32-key blocks (16 MFMAs, two chains). The
+  // K operands are read PF steps ahead so that LDS latency stays off the MFMA chain
+  // (sched_barrier keeps the compiler from sinking the reads next to their use).
+  f32x16_t sacc[2];
+  auto scores = [&](auto st_tag) {
+    constexpr uint32_t SOFF = decltype(st_tag)::value * 2 * TILE;
+    constexpr int PF = 3;
+    auto kread = [&](int s, int mb) {
+      return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
+          koff[s] + SOFF + mb * 32 * ROWB);
+    };
+    u32x4_t ka[PF + 1][2];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      ka[s][0] = kread(s, 0);
+      ka[s][1] = kread(s, 1);
+    }
+    sacc[0] = f32x16_t{};
+    sacc[1] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s + PF < 8) {
+        ka[(s + PF) % (PF + 1)][0] = kread(s + PF, 0);
+        ka[(s + PF) % (PF + 1)][1] = kread(s + PF, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, ka[s % (PF + 1)][mb]),
+            __builtin_bit_cast(bf16x8_t, qop[s]), sacc[mb], 0, 0, 0);
     }
   };
 
-  auto compute_tile = [&](int kt, int st, bool diag) {
-    const char* ks = smem[st][0];
-    const char* vs = smem[st][1];
-    // ---- S^T = K Q^T : two 32-key blocks ----
-    f32x16_t sacc[2];
+  // Online softmax of tile kt's scores (raw; scale * log2(e) is applied inside the
+  // exponent, so the running max m_run is in scaled log2 units) into P (bf16, the B
+  // operand of PV), with the causal mask on the tile that holds the diagonal.
+  u32x4_t pop[4];
+  auto softmax = [&](int kt, bool diag) {
+    if (diag) {
+      const int lim = my_q - kt * BN - 4 * half;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sacc[mb] = f32x16_t{};
-      const int row = 32 * mb + l32;
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4_t a = *(const u32x4_t*)(ks + row * ROWB + (((2 * s + half) ^ k_swz(row)) << 4));
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                           __builtin_bit_cast(bf16x8_t, qop[s]),
-                                                           sacc[mb], 0, 0, 0);
-      }
+        for (int j = 0; j < 16; ++j)
+          if (32 * mb + 8 * (j >> 2) + (j & 3) > lim) sacc[mb][j] = -INFINITY;
     }
-    // ---- online softmax on this lane's query ----
-    float sv[2][16];
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float x = sacc[mb][j] * scale_log2;
-        if (diag) {
-          const int key = kt * BN + 32 * mb + 8 * (j >> 2) + 4 * half + (j & 3);
-          x = key > my_q ? -INFINITY : x;
-        }
-        sv[mb][j] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[mb][j]);
+    {  // the other half-wave holds the other keys of each 8-key group: swap halves
+      const u32x2_t r = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                    false, false));
+      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * sl2;
+    }
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new > m_run + kLazy) ? m_new : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_use;
     float psum = 0.f;
-    u32x4_t pop[4];
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp) {
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(sv[sp >> 1][8 * (sp & 1) + i] - m_use);
+        pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][8 * (sp & 1) + i], sl2, -m_use));
         psum += pv[i];
       }
       pop[sp] = u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
@@ -165,47 +254,118 @@ __global__ __launch_bounds__(prefill::THREADS) void prefill_causal_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
     }
-    // ---- O^T += V^T P^T ----
-    const int g16 = lane >> 4;
-    const int i16 = lane & 15;
+  };
+
+  // O^T += V^T P^T with V from stage ST (16 MFMAs, four chains), transpose reads issued
+  // PF MFMAs ahead.
+  auto pv = [&](auto st_tag) {
+    constexpr uint32_t SOFF = decltype(st_tag)::value * 2 * TILE;
+    constexpr int PF = 3;
+    auto vread = [&](int i) {  // operand of MFMA i = 4 sp + mbd
+      const int sp = i >> 2, mbd = i & 3;
+      const uint32_t a0p = voff[mbd] + SOFF + (16 * sp) * ROWB;
+      const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)a0p);
+      const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(a0p + 8 * ROWB));
+      const u32x2_t a0 = __builtin_bit_cast(u32x2_t, t0);
+      const u32x2_t a1 = __builtin_bit_cast(u32x2_t, t1);
+      return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    };
+    u32x4_t va[PF + 1];
 #pragma unroll
-    for (int sp = 0; sp < 4; ++sp) {
+    for (int i = 0; i < PF; ++i) va[i] = vread(i);
 #pragma unroll
-      for (int mbd = 0; mbd < 4; ++mbd) {
-        const int chunk = 4 * mbd + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-        const int sub = (i16 & 1) * 8;
-        const int row0 = 16 * sp + 4 * (g16 >> 1) + (i16 >> 2);
-        const int row1 = row0 + 8;
-        const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t*)(vs + row0 * ROWB + ((chunk ^ v_swz(row0)) << 4) + sub));
-        const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t*)(vs + row1 * ROWB + ((chunk ^ v_swz(row1)) << 4) + sub));
-        const u32x2_t a0 = __builtin_bit_cast(u32x2_t, t0);
-        const u32x2_t a1 = __builtin_bit_cast(u32x2_t, t1);
-        const u32x4_t a = {a0[0], a0[1], a1[0], a1[1]};
-        oacc[mbd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                            __builtin_bit_cast(bf16x8_t, pop[sp]),
-                                                            oacc[mbd], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i + PF < 16) va[(i + PF) % (PF + 1)] = vread(i + PF);
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, va[i % (PF + 1)]),
+          __builtin_bit_cast(bf16x8_t, pop[i >> 2]), oacc[i & 3], 0, 0, 0);
     }
   };
 
-  // Same stage handshake as the decode kernel: per-wave vmcnt, then a bare barrier,
-  // so the next tile's DMA stays in flight while this one is used.
-  issue_tile(0, 0);
-  for (int kt = 0; kt < wg_tiles; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < wg_tiles) {
-      issue_tile(kt + 1, st ^ 1);
-      wait_vmcnt<LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    if (kt < wave_tiles) compute_tile(kt, st, kt == wave_tiles - 1);
+  // Two wave groups in antiphase. Waves 0-3 (group A) and 4-7 (group B) put one wave of
+  // each group on every SIMD. Time is cut into phases by workgroup barriers; in each phase
+  // one group runs its MFMA phase (PV of tile t, then the scores of tile t+1) while the
+  // other runs its softmax phase (VALU), so matrix and vector units of a SIMD work at the
+  // same time. Global phase p: group A runs softmax(t) at p = 2t+1 and MFMA(t) at
+  // p = 2t+2 (scores(0) at p = 0); group B runs one phase later. Hence K(t) is read in
+  // phases 2t, 2t+1 and V(t) in phases 2t+2, 2t+3. Tile t lives in stage t % 2; at every
+  // even phase 2u all waves issue the DMA of K(u+1) and V(u), whose stages were last read
+  // in phase 2u-1, and wait for it (vmcnt) before the barrier that opens phase 2u+2.
+  // Every wave passes 2 * wg_tiles + 2 barriers.
+  auto bar = [&]() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();
+  };
+  auto even_phase_dma = [&](int u, auto par_tag) {  // u % 2 == par
+    constexpr int PAR = decltype(par_tag)::value;
+    if (u + 1 < wg_tiles) issue_k(u + 1, PAR ^ 1);
+    if (u < wg_tiles) issue_v(u, PAR);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  // tile t (parity PAR) for a wave of group A: softmax at phase 2t+1, MFMA at 2t+2
+  auto tile_a = [&](int t, auto par_tag) {
+    constexpr int PAR = decltype(par_tag)::value;
+    bar();  // phase 2t+1
+    if (t < wave_tiles) softmax(t, t + 1 == wave_tiles);
+    wait_vmcnt<0>();
+    bar();  // phase 2t+2
+    even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
+    if (t < wave_tiles) pv(par_tag);
+    if (t + 1 < wave_tiles) scores(std::integral_constant<int, PAR ^ 1>{});
+  };
+  // tile t for a wave of group B: softmax at phase 2t+2, MFMA at 2t+3
+  auto tile_b = [&](int t, auto par_tag) {
+    constexpr int PAR = decltype(par_tag)::value;
+    wait_vmcnt<0>();
+    bar();  // phase 2t+2
+    even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
+    if (t < wave_tiles) softmax(t, t + 1 == wave_tiles);
+    bar();  // phase 2t+3
+    if (t < wave_tiles) pv(par_tag);
+    if (t + 1 < wave_tiles) scores(std::integral_constant<int, PAR ^ 1>{});
+  };
+
+  issue_k(0, 0);
+  // KV append: this workgroup copies the new K/V rows of its own positions
+  // [q0, q0 + BMPOS) of KV head kvh into their cache slots (slot pos % 16 of page
+  // page_table[b][pos / 16]); every position of every (b, kvh) is owned by exactly one
+  // workgroup. The rows were just requested by the first tile's DMA, so they come from L2.
+  {
+    const int nrows = min(BMPOS, S - q0);
+    for (int idx = (int)threadIdx.x; idx < nrows * 32; idx += THREADS) {
+      const int is_v = idx >= nrows * 16;
+      const int rem = idx - is_v * nrows * 16;
+      const int pos = q0 + (rem >> 4), c = rem & 15;
+      const int page = page_table[(size_t)b * max_pages + (pos >> 4)];
+      const u32x4_t x =
+          *(const u32x4_t*)((is_v ? v : k) + ((size_t)(b * S + pos) * Hkv + kvh) * D + c * 8);
+      *(u32x4_t*)((is_v ? v_cache : k_cache) + (((size_t)page * Hkv + kvh) * 16 + (pos & 15)) * D +
+                  c * 8) = x;
+    }
   }
+  wait_vmcnt<0>();  // K(0) has landed and the append's stores have completed
+  bar();  // phase 0
+  even_phase_dma(0, P0{});
+  if (w < 4) {
+    if (wave_tiles > 0) scores(P0{});
+    for (int t = 0; t < wg_tiles; t += 2) {
+      tile_a(t, P0{});
+      if (t + 1 < wg_tiles) tile_a(t + 1, P1{});
+    }
+    bar();
+  } else {
+    bar();  // phase 1
+    if (wave_tiles > 0) scores(P0{});
+    for (int t = 0; t < wg_tiles; t += 2) {
+      tile_b(t, P0{});
+      if (t + 1 < wg_tiles) tile_b(t + 1, P1{});
+    }
+  }
+  wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T / l, bf16, 4 consecutive dims per store ----
   if (wave_tiles == 0 || my_q >= S) return;
@@ -224,25 +384,28 @@ __global__ __launch_bounds__(prefill::THREADS) void prefill_causal_kernel(
 }
 
 template <int G>
-static int launch_g(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
+static int launch_g(const void* q, const void* k, const void* v, void* out, void* k_cache,
+                    void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
                     int Hkv, float scale, hipStream_t s) {
   constexpr int BMPOS = 256 / G;
   const int n_qtiles = (S + BMPOS - 1) / BMPOS;
   dim3 grid((unsigned)(B * Hkv), (unsigned)n_qtiles);
   hipLaunchKernelGGL((prefill_causal_kernel<G>), grid, dim3(prefill::THREADS), 0, s,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)out, S, Hq,
-                     Hkv, scale * kLog2e, n_qtiles);
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)out,
+                     (bf16_t*)k_cache, (bf16_t*)v_cache, page_table, max_pages, S, Hq, Hkv,
+                     scale * kLog2e, n_qtiles);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
-int launch_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
+int launch_prefill(const void* q, const void* k, const void* v, void* out, void* k_cache,
+                   void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s) {
   if (D != prefill::D) return GQA_ERR_UNSUPPORTED;
   switch (Hq / Hkv) {
-    case 1: return launch_g<1>(q, k, v, out, B, S, Hq, Hkv, scale, s);
-    case 2: return launch_g<2>(q, k, v, out, B, S, Hq, Hkv, scale, s);
-    case 4: return launch_g<4>(q, k, v, out, B, S, Hq, Hkv, scale, s);
-    case 8: return launch_g<8>(q, k, v, out, B, S, Hq, Hkv, scale, s);
+    case 1: return launch_g<1>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
+    case 2: return launch_g<2>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
+    case 4: return launch_g<4>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
+    case 8: return launch_g<8>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
     default: return GQA_ERR_UNSUPPORTED;
   }
 }

@@ -95,3 +95,17 @@ def test_config3_deterministic(gpu_lib, cfg3):
     b = _run(gpu_lib, x)
     assert torch.equal(a, b)
     assert torch.isfinite(a.float()).all()
+
+
+@pytest.mark.parametrize("scale", [-0.0884, 0.5, 0.0])
+def test_prefill_scale_sign_and_magnitude(gpu_lib, scale):
+    """The row max is taken on unscaled scores and the scale applied in the exponent;
+    a negative scale (max becomes min), a large one (sharp softmax, many rescales) and
+    zero (uniform weights, the running mean of V) must all match the oracle."""
+    print(f"[prefill] scale {scale}", flush=True)
+    x = synth.prefill_inputs(2, 200, 8, 2, 128, 16, seed=77, device=DEV)
+    x.scale = scale
+    out = _run(gpu_lib, x)
+    c = x.to("cpu")
+    ref = oracle.prefill_causal(c.q, c.k, c.v, scale)
+    assert_close(out, ref, "bf16", f"prefill scale={scale}")
