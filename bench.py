@@ -45,8 +45,22 @@ def prefill_flops(B, S, hq, d) -> float:
     return 4.0 * d * S * (S + 1) / 2 * B * hq
 
 
+def event_times_queued(fn, n, stream):
+    """Per-call durations (ms) from HIP events around each of n calls enqueued back to back
+    (no host synchronisation in between, so the GPU never waits for the host)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
 def event_times(fn, n, stream, flush=None):
-    """Per-call durations (ms) from HIP events recorded on ``stream``."""
+    """Per-call durations (ms) from HIP events recorded on ``stream``, each call run alone
+    (after ``flush`` if given)."""
     ts = []
     for _ in range(n):
         if flush is not None:
@@ -112,6 +126,12 @@ def ceilings(g, dev, stream):
     f()
     t_read = statistics.median(event_times(f, 10, stream))
     del src
+    # a plain device copy of known size (512 MiB read + 512 MiB written): the reference that
+    # calibrates the rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+    a = torch.empty(2**27, dtype=torch.float32, device=dev)
+    a_copy = torch.empty_like(a)
+    a_copy.copy_(a)
+    del a, a_copy
     fs = torch.empty(1024 * 8, dtype=torch.float32, device=dev)
     blocks, iters = 1024, 4096
     h = lambda: g.bench_mfma_bf16(fs, blocks, iters)
@@ -245,7 +265,7 @@ def main():
         for _ in range(5):
             pstep()
         torch.cuda.synchronize()
-        pt = event_times(pstep, 30, stream)
+        pt = event_times_queued(pstep, 30, stream)
         pmed = statistics.median(pt)
         B, S, hq, d = p.q.shape
         fl = prefill_flops(B, S, hq, d)
