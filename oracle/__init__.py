@@ -36,6 +36,7 @@ and invariants.
 
 from .attention import (  # noqa: F401
     append_paged,
+    append_paged_at,
     combine_splits,
     decode_paged,
     decode_paged_rows,
@@ -45,6 +46,8 @@ from .attention import (  # noqa: F401
     kv_head_of,
     logical_to_physical,
     prefill_causal,
+    prefill_paged,
+    prefill_paged_rows,
     prefill_causal_rows,
     split_page_ranges,
 )

@@ -22,6 +22,13 @@ Readings (the pages leave these open):
   * prefill row i attends keys 0..i (causal, diagonal included), the new
     tokens being positions 0..S-1 ([GQA-BATCH] Figure 2 caption names the
     causal mask, nothing more);
+  * chunked prefill (a chunk of n_b new tokens appended to a sequence that
+    already holds p_b cached tokens; [TRT-GQA] section "动态形状与KV Cache管理"
+    has the cache grow by the new tokens) puts new row i at absolute position
+    p_b + i; it attends every cached key and the new keys up to itself
+    (keys 0..p_b+i: the causal mask of [GQA-BATCH] Figure 2 aligned to the
+    bottom-right corner); the new K/V rows are written at positions
+    p_b..p_b+n_b-1 before they are read;
   * NumSplits ([GQA-BATCH] section "核心参数调优") splits a sequence's pages
     into NS contiguous page ranges of ceil(np/NS) pages; each split yields a
     normalised partial output and a natural-log log-sum-exp; an empty split
@@ -294,4 +301,65 @@ def append_paged(cache, new, page_table, page_size: int):
         for j in range(S):
             p, s = logical_to_physical(pt[b], j, page_size)
             out[p, :, s, :] = new[b, j, :, :]
+    return out
+
+
+def append_paged_at(cache, new, page_table, past_lens, new_lens, page_size: int):
+    """Cache after writing new[b][i] at logical position past_lens[b] + i, i < new_lens[b].
+
+    ``new`` is [B][S][Hkv][D]; rows i >= new_lens[b] are ignored. Bit copy, as append_paged.
+    """
+    out = cache.clone() if torch is not None and isinstance(cache, torch.Tensor) else cache.copy()
+    pt = _i64(page_table)
+    past = _i64(past_lens)
+    nl = _i64(new_lens)
+    for b in range(new.shape[0]):
+        for i in range(int(nl[b])):
+            p, s = logical_to_physical(pt[b], int(past[b]) + i, page_size)
+            out[p, :, s, :] = new[b, i, :, :]
+    return out
+
+
+def prefill_paged_rows(q, k_cache, v_cache, k_new, v_new, page_table, past_lens, new_lens,
+                       scale: float, rows, page_size: int = 16):
+    """Chunked prefill outputs for the (b, h) pairs in ``rows``: dict -> [new_lens[b]][D].
+
+    Sequence b holds past_lens[b] tokens in the paged cache (``k_cache``, ``v_cache`` as
+    they were before the chunk; positions < past_lens[b] are read through page_table)
+    and appends new_lens[b] tokens whose K/V are k_new[b][:n], v_new[b][:n]. New row i is
+    the query at position p + i and attends keys 0..p+i (cached keys, then new keys).
+    """
+    B, S, hq, d = q.shape
+    hkv = k_new.shape[2]
+    pt = _i64(page_table)
+    past = _i64(past_lens)
+    nl = _i64(new_lens)
+    res = {}
+    for (b, h) in rows:
+        p, n = int(past[b]), int(nl[b])
+        kvh = kv_head_of(h, hq, hkv)
+        K = np.concatenate([_gather_rows(k_cache, pt[b], p, kvh, page_size),
+                            _f64(k_new[b, :n, kvh, :])], axis=0)
+        V = np.concatenate([_gather_rows(v_cache, pt[b], p, kvh, page_size),
+                            _f64(v_new[b, :n, kvh, :])], axis=0)
+        Q = _f64(q[b, :n, h, :])
+        scores = scale * (Q @ K.T)  # [n][p + n]
+        mask = np.arange(p + n)[None, :] > (p + np.arange(n))[:, None]
+        scores[mask] = -np.inf
+        m = scores.max(axis=1, keepdims=True)
+        w = np.exp(scores - m)
+        res[(b, h)] = (w @ V) / w.sum(axis=1, keepdims=True)
+    return res
+
+
+def prefill_paged(q, k_cache, v_cache, k_new, v_new, page_table, past_lens, new_lens,
+                  scale: float, page_size: int = 16) -> np.ndarray:
+    """Chunked prefill: [B][S][Hq][D] float64; rows i >= new_lens[b] are NaN (undefined)."""
+    B, S, hq, d = q.shape
+    out = np.full((B, S, hq, d), np.nan)
+    got = prefill_paged_rows(q, k_cache, v_cache, k_new, v_new, page_table, past_lens,
+                             new_lens, scale, [(b, h) for b in range(B) for h in range(hq)],
+                             page_size)
+    for (b, h), o in got.items():
+        out[b, :o.shape[0], h, :] = o
     return out

@@ -74,3 +74,38 @@ def prefill(q, k, v, scale):
             rows.append(heads)
         out.append(rows)
     return out
+
+
+def prefill_paged(q, k_pool, v_pool, k_new, v_new, page_table, past, new, scale):
+    """Chunked prefill on nested lists: sequence b holds past[b] cached tokens (pools
+    [page][kvh][slot][c] through page_table[b]) and appends new[b] tokens k_new/v_new[b][i];
+    new row i (position past[b] + i) attends keys 0..past[b]+i. -> out[b][i][h][c] for
+    i < new[b]."""
+    B = len(q)
+    hq = len(q[0][0])
+    hkv = len(k_new[0][0])
+    group = hq // hkv
+    page = len(k_pool[0][0])
+    d = len(q[0][0][0])
+    out = []
+    for b in range(B):
+        rows = []
+        for i in range(new[b]):
+            heads = []
+            for h in range(hq):
+                g = h // group
+                keys, vals = [], []
+                for j in range(past[b] + i + 1):
+                    if j < past[b]:
+                        p = page_table[b][j // page]
+                        keys.append(k_pool[p][g][j % page])
+                        vals.append(v_pool[p][g][j % page])
+                    else:
+                        keys.append(k_new[b][j - past[b]][g])
+                        vals.append(v_new[b][j - past[b]][g])
+                scores = [scale * math.fsum(q[b][i][h][c] * keys[t][c] for c in range(d))
+                          for t in range(len(keys))]
+                heads.append(_softmax_avg(scores, vals))
+            rows.append(heads)
+        out.append(rows)
+    return out

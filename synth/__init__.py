@@ -159,6 +159,69 @@ def prefill_inputs(B, S, Hq, Hkv, D, P, seed=0, *, pad_pages=64, dtype="bf16",
                          dict(seed=seed))
 
 
+@dataclass
+class ChunkedInputs:
+    q: torch.Tensor            # [B][S][Hq][D]: new rows i < new_lens[b] are live
+    k: torch.Tensor            # [B][S][Hkv][D]: K of the new tokens
+    v: torch.Tensor            # [B][S][Hkv][D]
+    k_cache: torch.Tensor      # [num_pages][Hkv][P][D]: the past_lens[b] cached tokens
+    v_cache: torch.Tensor
+    page_table: torch.Tensor   # [B][max_pages] int32, covers past_lens[b] + new_lens[b]
+    past_lens: torch.Tensor    # [B] int32
+    new_lens: torch.Tensor     # [B] int32, <= S
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    def to(self, device):
+        return ChunkedInputs(self.q.to(device), self.k.to(device), self.v.to(device),
+                             self.k_cache.to(device), self.v_cache.to(device),
+                             self.page_table.to(device), self.past_lens.to(device),
+                             self.new_lens.to(device), self.scale, dict(self.meta))
+
+
+def chunked_inputs(B, S, Hq, Hkv, D, P, past, new=None, seed=0, *, pad_pages=16, dtype="bf16",
+                   device="cpu", poison=True):
+    """Chunked prefill inputs: sequence b already holds past[b] tokens in the paged pool and
+    appends new[b] <= S tokens (default S). ``past`` / ``new``: an int or a list of B ints.
+
+    Draw order: Q, new K, new V, cached K, cached V, page permutation. Pool slots that no
+    cached token owns (the tail of the last cached page, the pages of the new tokens, pad
+    pages) hold NaN when ``poison``; the page table is padded with -1 past the live pages.
+    """
+    dt = DTYPES[dtype]
+    dev = torch.device(device)
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    past = [past] * B if isinstance(past, int) else list(past)
+    new = [S] * B if new is None else ([new] * B if isinstance(new, int) else list(new))
+    assert len(past) == B and len(new) == B and all(0 <= n <= S for n in new)
+    q = _randn((B, S, Hq, D), gen, dt, dev)
+    k = _randn((B, S, Hkv, D), gen, dt, dev)
+    v = _randn((B, S, Hkv, D), gen, dt, dev)
+    n_pages = [(p + n + P - 1) // P for p, n in zip(past, new)]
+    max_pages = max(max(n_pages), 1)
+    live = sum(n_pages)
+    num_pages = live + pad_pages
+    fill = float("nan") if poison else 0.0
+    k_cache = torch.full((num_pages, Hkv, P, D), fill, dtype=dt)
+    v_cache = torch.full((num_pages, Hkv, P, D), fill, dtype=dt)
+    kc = [_randn((p, Hkv, D), gen, dt, torch.device("cpu")) for p in past]
+    vc = [_randn((p, Hkv, D), gen, dt, torch.device("cpu")) for p in past]
+    perm = torch.randperm(live, generator=gen).to(torch.int32)
+    pt = torch.full((B, max_pages), -1, dtype=torch.int32)
+    o = 0
+    for b in range(B):
+        pt[b, :n_pages[b]] = perm[o:o + n_pages[b]]
+        o += n_pages[b]
+        for t in range(past[b]):
+            page, slot = int(pt[b, t // P]), t % P
+            k_cache[page, :, slot, :] = kc[b][t]
+            v_cache[page, :, slot, :] = vc[b][t]
+    return ChunkedInputs(q, k, v, k_cache.to(dev), v_cache.to(dev), pt.to(dev),
+                         torch.tensor(past, dtype=torch.int32, device=dev),
+                         torch.tensor(new, dtype=torch.int32, device=dev),
+                         1.0 / float(D) ** 0.5, dict(seed=seed))
+
+
 # ---- the five workloads ------------------------------------------------------------------
 
 def config1(device="cpu", **kw):

@@ -351,3 +351,86 @@ def test_planted_off_by_one_causal_is_caught(monkeypatch):
     got = oa.prefill_causal(x.q, x.k, x.v, x.scale)
     monkeypatch.undo()
     assert not _tol_close(got, ref)
+
+
+# ------------------------------------------------------------- chunked prefill
+
+CHUNKED = [
+    # B, S, Hq, Hkv, D, P, past, new
+    (1, 3, 2, 1, 8, 4, [0], [3]),
+    (2, 5, 4, 2, 8, 4, [1, 6], [5, 2]),
+    (2, 4, 4, 1, 4, 4, [4, 9], [1, 4]),
+    (1, 6, 2, 2, 8, 2, [3], [0]),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=lambda c: f"B{c[0]}-S{c[1]}-p{c[6]}-n{c[7]}")
+def test_chunked_prefill_matches_brute_force(case):
+    B, S, hq, hkv, D, P, past, new = case
+    x = synth.chunked_inputs(B, S, hq, hkv, D, P, past, new, seed=70 + S, dtype="f32")
+    got = oracle.prefill_paged(x.q, x.k_cache, x.v_cache, x.k, x.v, x.page_table, x.past_lens,
+                               x.new_lens, x.scale, P)
+    ref = brute.prefill_paged(x.q.double().tolist(), x.k_cache.double().tolist(),
+                              x.v_cache.double().tolist(), x.k.double().tolist(),
+                              x.v.double().tolist(), x.page_table.tolist(), past, new, x.scale)
+    for b in range(B):
+        if new[b]:
+            assert _tol_close(got[b, :new[b]], np.asarray(ref[b]))
+        assert np.isnan(got[b, new[b]:]).all()  # rows past the chunk are undefined
+
+
+def test_chunked_prefill_without_past_is_causal_prefill():
+    x = synth.chunked_inputs(2, 9, 4, 2, 16, 4, 0, None, seed=81, dtype="f32")
+    got = oracle.prefill_paged(x.q, x.k_cache, x.v_cache, x.k, x.v, x.page_table, x.past_lens,
+                               x.new_lens, x.scale, 4)
+    assert _tol_close(got, oracle.prefill_causal(x.q, x.k, x.v, x.scale))
+    # and its append is the plain append at positions 0..S-1
+    a = oracle.append_paged_at(x.k_cache, x.k, x.page_table, x.past_lens, x.new_lens, 4)
+    b = oracle.append_paged(x.k_cache, x.k, x.page_table, 4)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_chunked_prefill_single_token_is_decode_after_append():
+    past = [0, 5, 16, 23]
+    x = synth.chunked_inputs(4, 3, 8, 2, 16, 4, past, 1, seed=82, dtype="f32")
+    got = oracle.prefill_paged(x.q, x.k_cache, x.v_cache, x.k, x.v, x.page_table, x.past_lens,
+                               x.new_lens, x.scale, 4)
+    kc = oracle.append_paged_at(x.k_cache, x.k, x.page_table, x.past_lens, x.new_lens, 4)
+    vc = oracle.append_paged_at(x.v_cache, x.v, x.page_table, x.past_lens, x.new_lens, 4)
+    dec = oracle.decode_paged(x.q[:, 0], kc, vc, x.page_table, x.past_lens + 1, x.scale)
+    assert _tol_close(got[:, 0], dec)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
+def test_chunked_prefill_matches_torch_sdpa_bottom_right(hq, hkv):
+    """torch's SDPA in float64 with an explicit bottom-right causal mask on the gathered
+    context (a library routine independent of the oracle)."""
+    B, S, D, P = 2, 6, 16, 4
+    past, new = [7, 2], [6, 4]
+    x = synth.chunked_inputs(B, S, hq, hkv, D, P, past, new, seed=83 + hq, dtype="f32")
+    got = oracle.prefill_paged(x.q, x.k_cache, x.v_cache, x.k, x.v, x.page_table, x.past_lens,
+                               x.new_lens, x.scale, P)
+    for b in range(B):
+        p, n = past[b], new[b]
+        t = torch.arange(p)
+        pages = x.page_table[b, (t // P)].long()
+        K = torch.cat([x.k_cache[pages, :, t % P, :], x.k[b, :n]], 0).double()  # [p+n][Hkv][D]
+        V = torch.cat([x.v_cache[pages, :, t % P, :], x.v[b, :n]], 0).double()
+        Q = x.q[b, :n].double()
+        allowed = torch.arange(p + n)[None, :] <= (p + torch.arange(n))[:, None]
+        ref = F.scaled_dot_product_attention(Q.transpose(0, 1), K.transpose(0, 1),
+                                             V.transpose(0, 1), attn_mask=allowed,
+                                             scale=x.scale, enable_gqa=True)
+        assert np.abs(got[b, :n] - ref.transpose(0, 1).numpy()).max() <= 1e-12
+
+
+def test_chunked_append_leaves_other_slots_untouched():
+    x = synth.chunked_inputs(2, 4, 4, 2, 8, 4, [3, 6], [4, 2], seed=84, dtype="f32")
+    after = oracle.append_paged_at(x.k_cache, x.k, x.page_table, x.past_lens, x.new_lens, 4)
+    changed = ~((after == x.k_cache) | (torch.isnan(after) & torch.isnan(x.k_cache)))
+    # exactly the new rows (new_lens tokens x Hkv heads) changed
+    assert int(changed.any(-1).sum()) == (4 + 2) * 2
+    for b, (p, n) in enumerate([(3, 4), (6, 2)]):
+        for i in range(n):
+            page, slot = int(x.page_table[b, (p + i) // 4]), (p + i) % 4
+            assert torch.equal(after[page, :, slot, :], x.k[b, i])
