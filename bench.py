@@ -45,6 +45,12 @@ def prefill_flops(B, S, hq, d) -> float:
     return 4.0 * d * S * (S + 1) / 2 * B * hq
 
 
+def chunked_flops(past, new, hq, d) -> float:
+    """QK^T and PV flops of chunked prefill: new row i attends past + i + 1 keys, so
+    4*D*(n*p + n(n+1)/2) per (b, head); ``past`` / ``new`` are per-sequence lists."""
+    return sum(4.0 * d * (n * p + n * (n + 1) / 2) * hq for p, n in zip(past, new))
+
+
 def event_times_queued(fn, n, stream):
     """Per-call durations (ms) from HIP events around each of n calls enqueued back to back
     (no host synchronisation in between, so the GPU never waits for the host)."""
@@ -283,11 +289,40 @@ def main():
         }
         del p, pout
 
+        # chunked prefill over a paged context: 4 sequences with 4096 cached tokens each
+        # append a 512-token chunk (re-appending the same rows every call is idempotent)
+        past, new = [4096] * 4, [512] * 4
+        c = synth.chunked_inputs(4, 512, 32, 8, 128, 16, past, new, seed=6000, device=dev)
+        cout = torch.empty_like(c.q)
+
+        def cstep():
+            g.prefill_paged(c.q, c.k, c.v, c.k_cache, c.v_cache, c.page_table, c.past_lens,
+                            c.new_lens, scale=c.scale, out=cout)
+
+        for _ in range(5):
+            cstep()
+        torch.cuda.synchronize()
+        cmed = statistics.median(event_times_queued(cstep, 30, stream))
+        cfl = chunked_flops(past, new, 32, 128)
+        ctf = cfl / (cmed * 1e-3) / 1e12
+        line["chunked_prefill"] = {
+            "workload": "chunked prefill over a paged context, B=4, 4096 cached + 512 new tokens "
+                        "per sequence, Hq=32, Hkv=8, D=128, bf16, page 16, permuted pages",
+            "median_us": round(cmed * 1e3, 2),
+            "tflops": round(ctf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(ctf, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ctf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "append_at_kernel + prefill_causal_kernel<4, paged> (one call)"},
+            "flops_per_call": cfl,
+        }
+        del c, cout
+
     ceil = ceilings(g, dev, stream)
     line["measured_ceiling"] = dict(ceil, decode_frac_of_read=round(achieved / ceil["stream_read_gbs"], 4))
-    if "prefill" in line:
-        line["prefill"]["frac_of_mfma_ceiling"] = round(
-            line["prefill"]["tflops"] / ceil["mfma_bf16_tflops"], 4)
+    for key in ("prefill", "chunked_prefill"):
+        if key in line:
+            line[key]["frac_of_mfma_ceiling"] = round(line[key]["tflops"] / ceil["mfma_bf16_tflops"], 4)
 
     # ---------------- CPU baseline: the float64 oracle on the host ----------------
     if not args.no_cpu_baseline:

@@ -29,11 +29,13 @@ SIGNATURES = {
     "gqa_decode_paged_balanced": (_i, [_p] * 7 + [_sz] + [_i] * 7 + [_f, _i, _p]),
     "gqa_decode_balanced_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "gqa_prefill_causal": (_i, [_p] * 7 + [_i] * 8 + [_f, _i, _p]),
+    "gqa_prefill_paged": (_i, [_p] * 9 + [_i] * 8 + [_f, _i, _p]),
     "gqa_combine_splits": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "gqa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "gqa_status_string": (ctypes.c_char_p, [_i]),
     "gqa_validate_decode": (_i, [_p] * 8 + [_i] * 8 + [_f, _i]),
     "gqa_validate_prefill": (_i, [_p] * 7 + [_i] * 8 + [_f, _i]),
+    "gqa_validate_prefill_paged": (_i, [_p] * 9 + [_i] * 8 + [_f, _i]),
     "gqa_validate_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _i]),
     "gqa_gather_paged": (_i, [_p, _p, _p, _p] + [_i] * 7 + [_p]),
     "gqa_bench_stream_read": (_i, [_p, _sz, _p, _i, _i, _p]),
@@ -223,6 +225,39 @@ def prefill_causal(q, k, v, k_cache, v_cache, page_table, scale: float | None = 
                                 _ptr(page_table), _ptr(out), B, S, Hq, Hkv, D, P,
                                 page_table.shape[1], num_pages, scale, BF16, _stream(q.device))
     _check(st, "gqa_prefill_causal")
+    return out
+
+
+def prefill_paged(q, k, v, k_cache, v_cache, page_table, past_lens, new_lens,
+                  scale: float | None = None, out=None):
+    """Chunked prefill: sequence b holds past_lens[b] cached tokens and appends new_lens[b]
+    tokens (k/v rows) at positions past .. past+new-1; new row i attends keys 0..past+i.
+    Returns out [B][S][Hq][D] (rows i >= new_lens[b] untouched)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(past_lens, "past_lens", torch.int32, 1)
+    _need(new_lens, "new_lens", torch.int32, 1)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    num_pages, Hkv_c, P, Dc = k_cache.shape
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or Hkv_c != Hkv or Dc != D:
+        raise ValueError("prefill shapes do not match")
+    if past_lens.shape != (B,) or new_lens.shape != (B,):
+        raise ValueError("past_lens / new_lens must be [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.gqa_prefill_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(page_table), _ptr(past_lens), _ptr(new_lens), _ptr(out), B, S,
+                               Hq, Hkv, D, P, page_table.shape[1], num_pages, scale, BF16,
+                               _stream(q.device))
+    _check(st, "gqa_prefill_paged")
     return out
 
 

@@ -20,6 +20,10 @@ int launch_decode_balanced(const void* q, const void* k, const void* v, const in
 int launch_prefill(const void* q, const void* k, const void* v, void* out, void* k_cache,
                    void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s);
+int launch_prefill_paged(const void* q, const void* k, const void* v, void* out, void* k_cache,
+                         void* v_cache, const int32_t* page_table, const int32_t* past_lens,
+                         const int32_t* new_lens, int max_pages, int B, int S, int Hq, int Hkv,
+                         int D, float scale, hipStream_t s);
 }  // namespace gqa
 
 extern "C" int gqa_balanced_auto_splits(int B, int Hkv);
@@ -86,6 +90,17 @@ int gqa_prefill_causal(const void* q, const void* k, const void* v, void* k_cach
   // one kernel: attention plus the append of the new K/V rows into the cache
   return gqa::launch_prefill(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv,
                              D, scale, (hipStream_t)stream);
+}
+
+int gqa_prefill_paged(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                      const int32_t* page_table, const int32_t* past_lens,
+                      const int32_t* new_lens, void* out, int B, int S, int Hq, int Hkv, int D,
+                      int P, int max_pages, int num_pages, float scale, int dtype, void* stream) {
+  int st = gqa_validate_prefill_paged(q, k, v, k_cache, v_cache, page_table, past_lens, new_lens,
+                                      out, B, S, Hq, Hkv, D, P, max_pages, num_pages, scale, dtype);
+  if (st != GQA_OK) return st;
+  return gqa::launch_prefill_paged(q, k, v, out, k_cache, v_cache, page_table, past_lens, new_lens,
+                                   max_pages, B, S, Hq, Hkv, D, scale, (hipStream_t)stream);
 }
 
 int gqa_gather_paged(const void* cache, const int32_t* page_table, const int32_t* context_lens,

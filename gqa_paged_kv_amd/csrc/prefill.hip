@@ -69,11 +69,17 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t num_reco
 }
 }  // namespace prefill
 
-template <int G>
+// PAGED = false: causal prefill of S new tokens per sequence (positions 0..S-1); K/V tiles
+// are read from the new k / v, and the kernel also appends them to the cache.
+// PAGED = true: chunked prefill. Sequence b already holds past_lens[b] tokens in the cache
+// and its new_lens[b] new tokens (already appended by append_at_kernel) sit at positions
+// past .. past+new-1; new row i attends keys 0 .. past+i, all read from the paged cache.
+template <int G, bool PAGED>
 __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_causal_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache,
-    const int32_t* __restrict__ page_table, int max_pages, int S, int Hq, int Hkv,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ past_lens,
+    const int32_t* __restrict__ new_lens, int max_pages, int S, int Hq, int Hkv,
     float scale_log2, int n_qtiles) {
   using namespace prefill;
   constexpr int BMPOS = 256 / G;  // positions per q-tile
@@ -92,13 +98,26 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   const int half = lane >> 5;
   const int hl = w / PB;
   const int h = kvh * G + hl;
-  const int qa = q0 + 32 * (w % PB);  // first query position of this wave
-  const int my_q = qa + l32;          // the query this lane's softmax state belongs to
+  const int qa = q0 + 32 * (w % PB);  // first new row of this wave
+  const int my_q = qa + l32;          // the new row this lane's softmax state belongs to
 
-  const int wave_tiles = qa < S ? (min(qa + 31, S - 1)) / BN + 1 : 0;
-  const int wg_tiles = (min(q0 + BMPOS, S) - 1) / BN + 1;
+  // p: tokens already cached before this call's rows, n: live new rows (lengths clamped
+  // to what the page table row can address)
+  int p = 0, n = S;
+  if constexpr (PAGED) {
+    const int cap = max_pages * 16;
+    p = min(max(past_lens[b], 0), cap);
+    n = min(max(new_lens[b], 0), min(S, cap - p));
+    if (q0 >= n) return;  // the whole workgroup: no live row (before any barrier)
+  }
+  const int end = p + n;  // keys of the sequence after this call
+  const int my_pos = p + my_q;  // absolute position of this lane's query
+  const int wave_tiles = qa < n ? (p + min(qa + 31, n - 1)) / BN + 1 : 0;
+  const int wg_tiles = (p + min(q0 + BMPOS, n) - 1) / BN + 1;
+  const int mask_from = (p + qa) / BN;  // tiles before it are below every row of the wave
 
-  // K and V of (b, kvh) as raw buffers; token t's row starts at byte t * row_stride.
+  // K and V of (b, kvh) as raw buffers; token t's row starts at byte t * row_stride
+  // (PAGED: one buffer per (page, kv head) block, built per load).
   const uint32_t row_stride = (uint32_t)Hkv * ROWB;
   const size_t bkv_off = (size_t)b * S * Hkv * D + (size_t)kvh * D;
   const uint32_t extent = (uint32_t)(S - 1) * row_stride + ROWB;
@@ -114,7 +133,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   const float sl2 = fmaxf(fabsf(scale_log2), 1e-30f);
   u32x4_t qop[8];
   {
-    const bool ok = my_q < S;
+    const bool ok = my_q < n;
     const bf16_t* qrow = q + (((size_t)b * S + (ok ? my_q : 0)) * Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -143,19 +162,42 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     dma_last[ii] = (uint32_t)(S - 1) * row_stride + chunk * 16;
   }
   const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(smem0 + w * 1024);
+  // PAGED: a load moves 4 consecutive keys, which share one 16-key page. Its first key
+  // g0 (clamped onto end - 1) picks the page through the page table; a lane's key is
+  // clamped onto end - 1 too (that row exists: keys past the rows of this workgroup are
+  // masked, but their V must be finite), and its byte offset in the (page, kv head) block
+  // is slot * 256 + the swizzled chunk.
+  auto paged_dma = [&](const bf16_t* cache, int t, int ii, uint32_t lds) {
+    const int wi2 = (ii & 1) * WAVES + w;
+    const int g0 = t * BN + 4 * wi2;
+    const int gk = min(g0, end - 1);
+    const int page = page_table[(size_t)b * max_pages + (gk >> 4)];
+    const int key = min(g0 + (lane >> 4), end - 1);
+    const int chunk = (lane & 15) ^ (ii >= 2 ? v_swz(4 * wi2 + (lane >> 4)) : k_swz(4 * wi2 + (lane >> 4)));
+    const u32x4_t rsrc = make_rsrc(cache + ((size_t)page * Hkv + kvh) * 16 * D, 16 * ROWB);
+    buffer_dma16(rsrc, (uint32_t)((key & 15) * ROWB + chunk * 16), lds);
+  };
   auto issue_k = [&](int t, int st) {  // K tile t into stage st
     const uint32_t off = (uint32_t)t * BN * row_stride;
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-      buffer_dma16(k_rsrc, min(dma_off[ii] + off, dma_last[ii]),
-                   dma_lds + st * 2 * TILE + ii * WAVES * 1024);
+    for (int ii = 0; ii < 2; ++ii) {
+      if constexpr (PAGED)
+        paged_dma(k_cache, t, ii, dma_lds + st * 2 * TILE + ii * WAVES * 1024);
+      else
+        buffer_dma16(k_rsrc, min(dma_off[ii] + off, dma_last[ii]),
+                     dma_lds + st * 2 * TILE + ii * WAVES * 1024);
+    }
   };
   auto issue_v = [&](int t, int st) {  // V tile t into stage st
     const uint32_t off = (uint32_t)t * BN * row_stride;
 #pragma unroll
-    for (int ii = 2; ii < 4; ++ii)
-      buffer_dma16(v_rsrc, min(dma_off[ii] + off, dma_last[ii]),
-                   dma_lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
+    for (int ii = 2; ii < 4; ++ii) {
+      if constexpr (PAGED)
+        paged_dma(v_cache, t, ii, dma_lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
+      else
+        buffer_dma16(v_rsrc, min(dma_off[ii] + off, dma_last[ii]),
+                     dma_lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
+    }
   };
 
   // Per-lane LDS byte offsets, fixed for the whole kernel (stage, key block and row step
@@ -215,7 +257,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   u32x4_t pop[4];
   auto softmax = [&](int kt, bool diag) {
     if (diag) {
-      const int lim = my_q - kt * BN - 4 * half;
+      const int lim = my_pos - kt * BN - 4 * half;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -310,7 +352,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   auto tile_a = [&](int t, auto par_tag) {
     constexpr int PAR = decltype(par_tag)::value;
     bar();  // phase 2t+1
-    if (t < wave_tiles) softmax(t, t + 1 == wave_tiles);
+    if (t < wave_tiles) softmax(t, t >= mask_from);
     wait_vmcnt<0>();
     bar();  // phase 2t+2
     even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
@@ -323,13 +365,14 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     wait_vmcnt<0>();
     bar();  // phase 2t+2
     even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
-    if (t < wave_tiles) softmax(t, t + 1 == wave_tiles);
+    if (t < wave_tiles) softmax(t, t >= mask_from);
     bar();  // phase 2t+3
     if (t < wave_tiles) pv(par_tag);
     if (t + 1 < wave_tiles) scores(std::integral_constant<int, PAR ^ 1>{});
   };
 
   issue_k(0, 0);
+  if constexpr (!PAGED) {
   // KV append: this workgroup copies the new K/V rows of its own positions
   // [q0, q0 + BMPOS) of KV head kvh into their cache slots (slot pos % 16 of page
   // page_table[b][pos / 16]); every position of every (b, kvh) is owned by exactly one
@@ -347,7 +390,8 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
                   c * 8) = x;
     }
   }
-  wait_vmcnt<0>();  // K(0) has landed and the append's stores have completed
+  }
+  wait_vmcnt<0>();  // K(0) has landed (and the append's stores have completed)
   bar();  // phase 0
   even_phase_dma(0, P0{});
   if (w < 4) {
@@ -368,7 +412,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T / l, bf16, 4 consecutive dims per store ----
-  if (wave_tiles == 0 || my_q >= S) return;
+  if (wave_tiles == 0 || my_q >= n) return;
   const float l_tot = l_half + __shfl_xor(l_half, 32);
   const float inv = 1.0f / l_tot;
   bf16_t* orow = out + (((size_t)b * S + my_q) * Hq + h) * D;
@@ -383,31 +427,80 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     }
 }
 
-template <int G>
+// Chunked prefill, step 1: new[b][i] (i < new_lens[b]) -> cache slot of position
+// past_lens[b] + i; one thread per 16-byte chunk of a (row, kv head), K and V. Lengths are
+// clamped exactly as in the attention kernel.
+__global__ __launch_bounds__(256) void append_at_kernel(
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, bf16_t* __restrict__ k_cache,
+    bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ past_lens, const int32_t* __restrict__ new_lens, int S, int Hkv,
+    int max_pages) {
+  using namespace prefill;
+  const int b = blockIdx.y;
+  const int cap = max_pages * 16;
+  const int p = min(max(past_lens[b], 0), cap);
+  const int n = min(max(new_lens[b], 0), min(S, cap - p));
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // over [S][Hkv][16 chunks]
+  const int i = idx / (Hkv * 16);
+  if (i >= n) return;
+  const int kvh = (idx / 16) % Hkv, c = idx & 15;
+  const int pos = p + i;
+  const int page = page_table[(size_t)b * max_pages + (pos >> 4)];
+  const size_t src = ((size_t)(b * S + i) * Hkv + kvh) * D + c * 8;
+  const size_t dst = (((size_t)page * Hkv + kvh) * 16 + (pos & 15)) * D + c * 8;
+  *(u32x4_t*)(k_cache + dst) = *(const u32x4_t*)(k + src);
+  *(u32x4_t*)(v_cache + dst) = *(const u32x4_t*)(v + src);
+}
+
+template <int G, bool PAGED>
 static int launch_g(const void* q, const void* k, const void* v, void* out, void* k_cache,
-                    void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
-                    int Hkv, float scale, hipStream_t s) {
+                    void* v_cache, const int32_t* page_table, const int32_t* past_lens,
+                    const int32_t* new_lens, int max_pages, int B, int S, int Hq, int Hkv,
+                    float scale, hipStream_t s) {
   constexpr int BMPOS = 256 / G;
   const int n_qtiles = (S + BMPOS - 1) / BMPOS;
   dim3 grid((unsigned)(B * Hkv), (unsigned)n_qtiles);
-  hipLaunchKernelGGL((prefill_causal_kernel<G>), grid, dim3(prefill::THREADS), 0, s,
+  hipLaunchKernelGGL((prefill_causal_kernel<G, PAGED>), grid, dim3(prefill::THREADS), 0, s,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)out,
-                     (bf16_t*)k_cache, (bf16_t*)v_cache, page_table, max_pages, S, Hq, Hkv,
-                     scale * kLog2e, n_qtiles);
+                     (bf16_t*)k_cache, (bf16_t*)v_cache, page_table, past_lens, new_lens,
+                     max_pages, S, Hq, Hkv, scale * kLog2e, n_qtiles);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+template <bool PAGED>
+static int launch_any(const void* q, const void* k, const void* v, void* out, void* k_cache,
+                      void* v_cache, const int32_t* page_table, const int32_t* past_lens,
+                      const int32_t* new_lens, int max_pages, int B, int S, int Hq, int Hkv, int D,
+                      float scale, hipStream_t s) {
+  if (D != prefill::D) return GQA_ERR_UNSUPPORTED;
+  switch (Hq / Hkv) {
+    case 1: return launch_g<1, PAGED>(q, k, v, out, k_cache, v_cache, page_table, past_lens, new_lens, max_pages, B, S, Hq, Hkv, scale, s);
+    case 2: return launch_g<2, PAGED>(q, k, v, out, k_cache, v_cache, page_table, past_lens, new_lens, max_pages, B, S, Hq, Hkv, scale, s);
+    case 4: return launch_g<4, PAGED>(q, k, v, out, k_cache, v_cache, page_table, past_lens, new_lens, max_pages, B, S, Hq, Hkv, scale, s);
+    case 8: return launch_g<8, PAGED>(q, k, v, out, k_cache, v_cache, page_table, past_lens, new_lens, max_pages, B, S, Hq, Hkv, scale, s);
+    default: return GQA_ERR_UNSUPPORTED;
+  }
 }
 
 int launch_prefill(const void* q, const void* k, const void* v, void* out, void* k_cache,
                    void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s) {
+  return launch_any<false>(q, k, v, out, k_cache, v_cache, page_table, nullptr, nullptr,
+                           max_pages, B, S, Hq, Hkv, D, scale, s);
+}
+
+int launch_prefill_paged(const void* q, const void* k, const void* v, void* out, void* k_cache,
+                         void* v_cache, const int32_t* page_table, const int32_t* past_lens,
+                         const int32_t* new_lens, int max_pages, int B, int S, int Hq, int Hkv,
+                         int D, float scale, hipStream_t s) {
   if (D != prefill::D) return GQA_ERR_UNSUPPORTED;
-  switch (Hq / Hkv) {
-    case 1: return launch_g<1>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
-    case 2: return launch_g<2>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
-    case 4: return launch_g<4>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
-    case 8: return launch_g<8>(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv, scale, s);
-    default: return GQA_ERR_UNSUPPORTED;
-  }
+  const int chunks = S * Hkv * 16;
+  hipLaunchKernelGGL(append_at_kernel, dim3((unsigned)((chunks + 255) / 256), (unsigned)B),
+                     dim3(256), 0, s, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)k_cache,
+                     (bf16_t*)v_cache, page_table, past_lens, new_lens, S, Hkv, max_pages);
+  if (hipGetLastError() != hipSuccess) return GQA_ERR_LAUNCH;
+  return launch_any<true>(q, k, v, out, k_cache, v_cache, page_table, past_lens, new_lens,
+                          max_pages, B, S, Hq, Hkv, D, scale, s);
 }
 
 }  // namespace gqa

@@ -112,6 +112,25 @@ int gqa_validate_prefill(const void* q, const void* k, const void* v, const void
   return GQA_OK;
 }
 
+int gqa_validate_prefill_paged(const void* q, const void* k, const void* v, const void* k_cache,
+                               const void* v_cache, const int32_t* page_table,
+                               const int32_t* past_lens, const int32_t* new_lens, const void* out,
+                               int B, int S, int Hq, int Hkv, int D, int P, int max_pages,
+                               int num_pages, float scale, int dtype) {
+  if (!past_lens || !new_lens) return GQA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !k_cache || !v_cache || !page_table || !out) return GQA_ERR_INVALID_ARG;
+  if (S <= 0) return GQA_ERR_INVALID_ARG;
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  int st = check_common(B, Hq, Hkv, D, P, max_pages, num_pages, scale);
+  if (st != GQA_OK) return st;
+  if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (D != 128) return GQA_ERR_UNSUPPORTED;
+  if (!supported_prefill_group(Hq / Hkv)) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)S * Hq > INT32_MAX / 256) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages * P > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
 int gqa_validate_combine(const float* ws_o, const float* ws_lse, const void* out, int B, int Hq,
                          int D, int num_splits, int out_dtype) {
   if (!ws_o || !ws_lse || !out) return GQA_ERR_INVALID_ARG;

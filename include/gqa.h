@@ -136,6 +136,33 @@ int gqa_prefill_causal(const void* q, const void* k, const void* v, void* k_cach
                        float scale, int dtype, void* stream);
 
 /*
+ * Chunked prefill over an existing paged context. Sequence b already holds past_lens[b]
+ * tokens in the pool; this call appends its new_lens[b] <= S new tokens at positions
+ * past_lens[b] .. past_lens[b] + new_lens[b] - 1 (page "TensorRT对Grouped Query Attention的
+ * 支持进展", section "动态形状与KV Cache管理": the cache grows by the tokens of each step) and
+ * computes their attention: new row i, at position past_lens[b] + i, attends keys
+ * 0 .. past_lens[b] + i, i.e. every cached token and the new tokens up to itself (the causal
+ * mask of the caption of Figure 2 of page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践",
+ * aligned to the last key). past_lens = 0, new_lens = S is gqa_prefill_causal.
+ *
+ *   q          [B][S][Hq][D]   bf16; rows i >= new_lens[b] are ignored
+ *   k, v       [B][S][Hkv][D]  bf16, the new tokens (rows i >= new_lens[b] ignored)
+ *   k_cache,   [num_pages][Hkv][P][D] bf16; positions < past_lens[b] are read through the
+ *   v_cache    page table; on return (stream order) the new rows are in their slots, copied
+ *              bit for bit; nothing else is written.
+ *   page_table [B][max_pages] int32, the first ceil((past + new) / P) entries valid per row;
+ *              pages of different sequences must be distinct.
+ *   past_lens, [B] int32 DEVICE arrays. Clamped on the device to 0 <= past <= max_pages*P and
+ *   new_lens   0 <= new <= min(S, max_pages*P - past).
+ *   out        [B][S][Hq][D]   bf16; rows i < new_lens[b] written, the others untouched.
+ * Enqueues two kernels (the append, then the attention reading all K/V from the pool).
+ */
+int gqa_prefill_paged(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                      const int32_t* page_table, const int32_t* past_lens,
+                      const int32_t* new_lens, void* out, int B, int S, int Hq, int Hkv, int D,
+                      int P, int max_pages, int num_pages, float scale, int dtype, void* stream);
+
+/*
  * Merge split partials: M = max_s lse_s, w_s = exp(lse_s - M),
  * out = sum_s w_s o_s / sum_s w_s; a row whose splits are all -inf is zero.
  *   ws_o [B][Hq][num_splits][D] fp32, ws_lse [B][Hq][num_splits] fp32
@@ -157,6 +184,11 @@ int gqa_validate_prefill(const void* q, const void* k, const void* v, const void
                          const void* v_cache, const int32_t* page_table, const void* out, int B,
                          int S, int Hq, int Hkv, int D, int P, int max_pages, int num_pages,
                          float scale, int dtype);
+int gqa_validate_prefill_paged(const void* q, const void* k, const void* v, const void* k_cache,
+                               const void* v_cache, const int32_t* page_table,
+                               const int32_t* past_lens, const int32_t* new_lens, const void* out,
+                               int B, int S, int Hq, int Hkv, int D, int P, int max_pages,
+                               int num_pages, float scale, int dtype);
 int gqa_validate_combine(const float* ws_o, const float* ws_lse, const void* out, int B, int Hq,
                          int D, int num_splits, int out_dtype);
 

@@ -194,9 +194,10 @@ def chunked_inputs(B, S, Hq, Hkv, D, P, past, new=None, seed=0, *, pad_pages=16,
     past = [past] * B if isinstance(past, int) else list(past)
     new = [S] * B if new is None else ([new] * B if isinstance(new, int) else list(new))
     assert len(past) == B and len(new) == B and all(0 <= n <= S for n in new)
-    q = _randn((B, S, Hq, D), gen, dt, dev)
-    k = _randn((B, S, Hkv, D), gen, dt, dev)
-    v = _randn((B, S, Hkv, D), gen, dt, dev)
+    cpu = torch.device("cpu")  # drawn on the host (same values for every device)
+    q = _randn((B, S, Hq, D), gen, dt, cpu)
+    k = _randn((B, S, Hkv, D), gen, dt, cpu)
+    v = _randn((B, S, Hkv, D), gen, dt, cpu)
     n_pages = [(p + n + P - 1) // P for p, n in zip(past, new)]
     max_pages = max(max(n_pages), 1)
     live = sum(n_pages)
@@ -216,7 +217,8 @@ def chunked_inputs(B, S, Hq, Hkv, D, P, past, new=None, seed=0, *, pad_pages=16,
             page, slot = int(pt[b, t // P]), t % P
             k_cache[page, :, slot, :] = kc[b][t]
             v_cache[page, :, slot, :] = vc[b][t]
-    return ChunkedInputs(q, k, v, k_cache.to(dev), v_cache.to(dev), pt.to(dev),
+    return ChunkedInputs(q.to(dev), k.to(dev), v.to(dev), k_cache.to(dev), v_cache.to(dev),
+                         pt.to(dev),
                          torch.tensor(past, dtype=torch.int32, device=dev),
                          torch.tensor(new, dtype=torch.int32, device=dev),
                          1.0 / float(D) ** 0.5, dict(seed=seed))

@@ -116,6 +116,29 @@ def test_prefill_validation_rules(lib):
     assert _vp(lib, P=8) == g.ERR_UNSUPPORTED
 
 
+def _vpp(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, pt=FAKE, past=FAKE, new=FAKE, out=FAKE,
+             B=4, S=512, Hq=32, Hkv=8, D=128, P=16, max_pages=8, num_pages=512, scale=0.088,
+             dtype=g.BF16)
+    a.update(kw)
+    return lib.gqa_validate_prefill_paged(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["pt"],
+                                          a["past"], a["new"], a["out"], a["B"], a["S"], a["Hq"],
+                                          a["Hkv"], a["D"], a["P"], a["max_pages"],
+                                          a["num_pages"], a["scale"], a["dtype"])
+
+
+def test_chunked_prefill_validation_rules(lib):
+    assert _vpp(lib) == g.OK  # max_pages * P < S is allowed: lengths are clamped on device
+    for k in ("q", "k", "v", "kc", "vc", "pt", "past", "new", "out"):
+        assert _vpp(lib, **{k: None}) == g.ERR_INVALID_ARG, k
+    assert _vpp(lib, S=0) == g.ERR_INVALID_ARG
+    assert _vpp(lib, Hq=30) == g.ERR_INVALID_ARG
+    assert _vpp(lib, dtype=g.F32) == g.ERR_UNSUPPORTED
+    assert _vpp(lib, Hq=32, Hkv=1) == g.ERR_UNSUPPORTED  # G = 32 not built for prefill
+    assert _vpp(lib, D=64) == g.ERR_UNSUPPORTED
+    assert _vpp(lib, P=32) == g.ERR_UNSUPPORTED
+
+
 def test_combine_validation_rules(lib):
     v = lib.gqa_validate_combine
     assert v(FAKE, FAKE, FAKE, 4, 32, 128, 8, g.BF16) == g.OK
@@ -133,6 +156,9 @@ def test_entry_points_reject_before_enqueueing(lib):
     st = lib.gqa_prefill_causal(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 8, 2, 128, 16,
                                 4, 8, 0.1, g.F32, None)
     assert st == g.ERR_UNSUPPORTED
+    st = lib.gqa_prefill_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 64, 8,
+                               2, 128, 16, 4, 8, 0.1, g.BF16, None)
+    assert st == g.ERR_INVALID_ARG
     st = lib.gqa_combine_splits(FAKE, None, FAKE, 1, 8, 128, 2, g.BF16, None)
     assert st == g.ERR_INVALID_ARG
     st = lib.gqa_gather_paged(FAKE, FAKE, FAKE, FAKE, 1, 2, 96, 16, 4, 8, g.BF16, None)
