@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kRegsThreads) void decode_regs_kernel(
   const char* v_base = (const char*)v_cache + (size_t)kvh * S::PAGE + r * S::ROW;
 
   WaveState<T, D, HW> st;
-  st.init(q + ((size_t)b * Hq + (active ? kvh : 0) * G) * D, qd);
+  st.init(q + ((size_t)b * Hq + (active ? kvh : 0) * G) * D, qd, scale_log2 < 0.f);
 
   uint32_t kb[2][4][W32], vb[2][4][W32];
   auto load_page = [&](int buf, int lp) {
@@ -149,9 +149,9 @@ __global__ __launch_bounds__(kRegsThreads) void decode_regs_kernel(
   auto run = [&](int buf, int lp) {
     const int tok0 = lp * kPage + r;
     if (lp + 1 < sr.lp1) {
-      st.template page<false>(kb[buf], vb[buf], tok0, sr.t_end, scale_log2);
+      st.template page<false>(kb[buf], vb[buf], tok0, sr.t_end, abs_scale(scale_log2));
     } else {
-      st.template page<true>(kb[buf], vb[buf], tok0, sr.t_end, scale_log2);
+      st.template page<true>(kb[buf], vb[buf], tok0, sr.t_end, abs_scale(scale_log2));
     }
   };
   if (active) {
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_lds_kernel(
   const char* v_base = (const char*)v_cache + (size_t)kvh * S::PAGE;
 
   WaveState<T, D, S::HW> st;
-  st.init(q + ((size_t)b * Hq + kvh * G + hg * S::HW) * D, qd);
+  st.init(q + ((size_t)b * Hq + kvh * G + hg * S::HW) * D, qd, scale_log2 < 0.f);
 
   // Page ids: scalar loads of the NEXT tile's ids go out with this tile's DMA, so the
   // issue path never waits on the page table. Entries past the split are replaced by
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_lds_kernel(
           load_row<T, D>(stage + j * S::PAGE + (4 * i + r) * S::ROW, qd, kw[i]);
           load_row<T, D>(stage + (NP + j) * S::PAGE + (4 * i + r) * S::ROW, qd, vw[i]);
         }
-        st.template page<MASKED>(kw, vw, lp * kPage + r, sr.t_end, scale_log2);
+        st.template page<MASKED>(kw, vw, lp * kPage + r, sr.t_end, abs_scale(scale_log2));
       }
     }
   };

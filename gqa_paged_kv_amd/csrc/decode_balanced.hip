@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
 
   WaveState<T, D, G> st;
   long seg_start = lo;  // first item of the current segment
-  st.init(q + ((size_t)b * Hq + kvh * G) * D, qd);
+  st.init(q + ((size_t)b * Hq + kvh * G) * D, qd, scale_log2 < 0.f);
   int T_b = min(context_lens[b], max_pages * kPage);
 
   auto store_row = [&](T* dst, int hw, float inv) {
@@ -196,16 +196,16 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   auto consume = [&](int buf, long i) {
     const int tok0 = pg * kPage + r;
     if (pg + 1 < np) {
-      st.template page<false>(kb[buf], vb[buf], tok0, T_b, scale_log2);
+      st.template page<false>(kb[buf], vb[buf], tok0, T_b, abs_scale(scale_log2));
     } else {
-      st.template page<true>(kb[buf], vb[buf], tok0, T_b, scale_log2);
+      st.template page<true>(kb[buf], vb[buf], tok0, T_b, abs_scale(scale_log2));
     }
     const bool unit_end = pg + 1 == np;
     if (unit_end || i + 1 == hi) finish(i);
     advance(b, kvh, pg, np);
     if (unit_end && i + 1 < hi) {
       seg_start = i + 1;
-      st.init(q + ((size_t)b * Hq + kvh * G) * D, qd);
+      st.init(q + ((size_t)b * Hq + kvh * G) * D, qd, scale_log2 < 0.f);
       T_b = min(context_lens[b], max_pages * kPage);
     }
   };

@@ -95,10 +95,16 @@ struct WaveState {
   uint32_t qw[HW][W32];
   float m[HW], l[HW], acc[HW][E];
 
-  __device__ __forceinline__ void init(const T* q_head0, int qd) {
+  // neg: the caller's scale is negative; q is negated here (exact) and the kernel runs with
+  // |scale| (see abs_scale), so the row max taken on raw q.k stays the max of the scaled
+  // scores.
+  __device__ __forceinline__ void init(const T* q_head0, int qd, bool neg) {
+    const uint32_t flip = neg ? (kBf16 ? 0x80008000u : 0x80000000u) : 0u;
 #pragma unroll
     for (int hw = 0; hw < HW; ++hw) {
       load_row<T, D>((const char*)(q_head0 + (size_t)hw * D), qd, qw[hw]);
+#pragma unroll
+      for (int x = 0; x < W32; ++x) qw[hw][x] ^= flip;
       m[hw] = -INFINITY;
       l[hw] = 0.f;
 #pragma unroll
@@ -221,6 +227,13 @@ struct WaveState {
     }
   }
 };
+
+// The scale the kernels run with: |scale * log2 e| (a negative scale is moved onto q by
+// WaveState::init), raised to 1e-30 so that dead slots (-inf) still give exp2 = 0 when the
+// caller's scale is 0 (every live weight is then exp2(~0) = 1, the uniform weights of 0).
+__device__ __forceinline__ float abs_scale(float scale_log2) {
+  return fmaxf(fabsf(scale_log2), 1e-30f);
+}
 
 // Page-aligned token range of split `split` of sequence b: pages [lp0, lp1), tokens < t_end.
 struct SplitRange {

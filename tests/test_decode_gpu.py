@@ -308,3 +308,22 @@ def test_balanced_config5(gpu_lib, B, Hkv):
     got = np.stack([to_f64(out[b, h]) for (b, h) in rows])
     want = np.stack([ref[r] for r in rows])
     assert_close(got, want, "bf16", f"balanced config5 B={B} Hkv={Hkv}")
+
+
+# ---------------------------------------------------------------- scale sign and magnitude
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.7])
+@pytest.mark.parametrize("path", ["split1", "split3", "balanced", "balanced_g16"])
+def test_decode_scale_sign_and_magnitude(gpu_lib, scale, path):
+    """The kernels take the row max of raw q.k and apply the scale in the exponent; a negative
+    scale (the max becomes the min), a zero scale (uniform weights; dead slots must still get
+    weight 0) and a large one must all match the oracle. Ragged lengths leave dead slots."""
+    print(f"[decode] scale {scale} {path}", flush=True)
+    hq, hkv = (32, 2) if path == "balanced_g16" else (8, 2)
+    x = synth.decode_inputs(3, hq, hkv, 128, 16, [37, 200, 5], "bf16", seed=91, device=DEV)
+    x.scale = scale
+    if path.startswith("split"):
+        out = _run(gpu_lib, x, ns=int(path[-1]))
+    else:
+        out = _run_bal(gpu_lib, x)
+    assert_close(out, _ref(x), "bf16", f"decode scale={scale} {path}")
