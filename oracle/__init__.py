@@ -34,6 +34,7 @@ against brute force, closed forms, a library routine (torch SDPA in float64)
 and invariants.
 """
 
+from .fp8 import decode_paged_fp8, dequantize  # noqa: F401
 from .attention import (  # noqa: F401
     append_paged,
     append_paged_at,

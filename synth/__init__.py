@@ -159,6 +159,57 @@ def prefill_inputs(B, S, Hq, Hkv, D, P, seed=0, *, pad_pages=64, dtype="bf16",
                          dict(seed=seed))
 
 
+FP8_DTYPES = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+@dataclass
+class Fp8DecodeInputs:
+    q: torch.Tensor            # [B][Hq][D] bf16
+    k_cache: torch.Tensor      # [num_pages][Hkv][P][D] uint8 (fp8 bytes)
+    v_cache: torch.Tensor      # [num_pages][Hkv][P][D] uint8
+    k_scale: float             # value of a K byte x = k_scale * fp8(x)
+    v_scale: float
+    page_table: torch.Tensor   # [B][max_pages] int32
+    context_lens: torch.Tensor  # [B] int32
+    scale: float
+    fmt: str                   # "e4m3" or "e5m2"
+    meta: dict = field(default_factory=dict)
+
+    def to(self, device):
+        return Fp8DecodeInputs(self.q.to(device), self.k_cache.to(device),
+                               self.v_cache.to(device), self.k_scale, self.v_scale,
+                               self.page_table.to(device), self.context_lens.to(device),
+                               self.scale, self.fmt, dict(self.meta))
+
+
+def fp8_decode_inputs(B, Hq, Hkv, D, P, lens, fmt="e4m3", seed=0, device="cpu", **kw):
+    """Decode inputs with an 8-bit KV pool: the fp32 draw of ``decode_inputs`` (same seed,
+    NaN in dead slots), q rounded to bf16, K and V divided by a per-tensor scale that maps
+    their largest magnitude to the format's largest finite value and rounded to the format
+    by torch (round to nearest even); the pools hold the raw bytes."""
+    x = decode_inputs(B, Hq, Hkv, D, P, lens, "f32", seed=seed, device="cpu", **kw)
+    ft = FP8_DTYPES[fmt]
+
+    def quant(c):
+        amax = float(torch.nan_to_num(c.abs(), nan=0.0).max())
+        sc = amax / FP8_MAX[fmt] if amax > 0 else 1.0
+        return (c / sc).to(ft).view(torch.uint8), sc
+
+    kq, ks = quant(x.k_cache)
+    vq, vs = quant(x.v_cache)
+    dev = torch.device(device)
+    return Fp8DecodeInputs(x.q.to(torch.bfloat16).to(dev), kq.to(dev), vq.to(dev), ks, vs,
+                           x.page_table.to(dev), x.context_lens.to(dev), x.scale, fmt,
+                           dict(x.meta, fmt=fmt))
+
+
+def config2_fp8(fmt="e4m3", device="cpu"):
+    """Workload 2 with an 8-bit KV pool: B=64, Hq=32, Hkv=8, D=128, P=16,
+    T ~ U{512..4096} (seed 2000, the same lengths and page table)."""
+    return fp8_decode_inputs(64, 32, 8, 128, 16, (512, 4096), fmt, seed=2000, device=device)
+
+
 @dataclass
 class ChunkedInputs:
     q: torch.Tensor            # [B][S][Hq][D]: new rows i < new_lens[b] are live

@@ -434,3 +434,49 @@ def test_chunked_append_leaves_other_slots_untouched():
         for i in range(n):
             page, slot = int(x.page_table[b, (p + i) // 4]), (p + i) % 4
             assert torch.equal(after[page, :, slot, :], x.k[b, i])
+
+
+# ------------------------------------------------------------- 8-bit KV cache
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_decoders_match_torch_for_every_byte(fmt, tdt):
+    """The bit-level decoders against torch's float8 types (a library routine), all 256 bytes."""
+    b = torch.arange(256, dtype=torch.uint8)
+    ref = b.view(tdt).to(torch.float64).numpy()
+    got = oracle.fp8.DECODERS[fmt](b.numpy())
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), np.where(~same)
+
+
+def test_fp8_decoder_special_values():
+    d4, d5 = oracle.fp8.decode_e4m3, oracle.fp8.decode_e5m2
+    assert d4(np.array([0x7E]))[0] == 448.0 and np.isnan(d4(np.array([0x7F]))[0])
+    assert d4(np.array([0x01]))[0] == 2.0 ** -9 and d4(np.array([0xB8]))[0] == -1.0
+    assert d5(np.array([0x7B]))[0] == 57344.0 and np.isinf(d5(np.array([0x7C]))[0])
+    assert d5(np.array([0x01]))[0] == 2.0 ** -16 and d5(np.array([0x3C]))[0] == 1.0
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_decode_matches_brute_force(fmt):
+    """Tiny 8-bit decode against the pure-Python brute force on values dequantized by torch."""
+    x = synth.fp8_decode_inputs(2, 4, 2, 16, 4, [7, 10], fmt, seed=55)
+    got = oracle.decode_paged_fp8(x.q, x.k_cache, x.v_cache, x.k_scale, x.v_scale,
+                                  x.page_table, x.context_lens, x.scale, fmt)
+    tdt = synth.FP8_DTYPES[fmt]
+    kd = (x.k_cache.view(tdt).double() * x.k_scale).tolist()
+    vd = (x.v_cache.view(tdt).double() * x.v_scale).tolist()
+    ref = brute.decode(x.q.double().tolist(), kd, vd, x.page_table.tolist(),
+                       x.context_lens.tolist(), x.scale)
+    assert _tol_close(got, ref)
+
+
+def test_fp8_quantisation_is_close_to_the_unquantised_decode():
+    """Sanity of the synthetic inputs: e4m3 keeps 3 mantissa bits, so the 8-bit decode is
+    within a few percent of the fp32 decode it was quantised from."""
+    x = synth.fp8_decode_inputs(2, 8, 2, 64, 16, [100, 37], "e4m3", seed=56)
+    f = synth.decode_inputs(2, 8, 2, 64, 16, [100, 37], "f32", seed=56)
+    a = oracle.decode_paged_fp8(x.q, x.k_cache, x.v_cache, x.k_scale, x.v_scale,
+                                x.page_table, x.context_lens, x.scale, "e4m3")
+    b = oracle.decode_paged(f.q.to(torch.bfloat16), f.k_cache, f.v_cache, f.page_table,
+                            f.context_lens, f.scale)
+    assert np.abs(a - b).max() < 0.1
