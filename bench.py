@@ -155,6 +155,7 @@ def main():
     ap.add_argument("--splits", type=int, default=DEFAULT_SPLITS)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="extra lines for the split/batch sweeps")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -258,6 +259,35 @@ def main():
         },
     }
     del scratch
+
+    # ---------------- decode over an 8-bit KV pool (workload 2, E4M3) ----------------
+    if not args.no_fp8:
+        f8 = synth.config2_fp8("e4m3", device=dev)
+        f8out = torch.empty_like(f8.q)
+        f8ws = g.balanced_workspace(B, Hq, Hkv, D, dev)
+        f8bytes = int(f8.context_lens.sum()) * Hkv * D * 1 * 2
+
+        def f8step():
+            g.decode_paged_fp8(f8.q, f8.k_cache, f8.v_cache, f8.k_scale, f8.v_scale,
+                               f8.page_table, f8.context_lens, fmt="e4m3", scale=f8.scale,
+                               out=f8out, workspace=f8ws)
+
+        for _ in range(10):
+            f8step()
+        torch.cuda.synchronize()
+        f8med = statistics.median(event_times_queued(f8step, 100, stream))
+        f8gbs = f8bytes / (f8med * 1e-3) / 1e9
+        line["decode_fp8"] = {
+            "workload": "paged GQA decode, workload 2 shape (B=64, Hq=32, Hkv=8, D=128, page 16, "
+                        "T~U[512,4096]) with an E4M3 KV pool (per-tensor scales), bf16 q/out",
+            "kv_bytes_per_call": f8bytes,
+            "median_us": round(f8med * 1e3, 2),
+            "gbs": round(f8gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(f8gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(f8gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "balanced_kernel<bf16,128,4,fp8e4m3> + fixup_kernel"},
+        }
+        del f8, f8out, f8ws
 
     # ---------------- prefill workload ----------------
     if not args.no_prefill:

@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgqa.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
+_FP8_CODE = {"e4m3": FP8_E4M3, "e5m2": FP8_E5M2}
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16}
 
 # Exported symbols and their C signatures (argument types in order).
@@ -28,12 +29,14 @@ SIGNATURES = {
     "gqa_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _p, _p] + [_i] * 8 + [_f, _i, _p]),
     "gqa_decode_paged_balanced": (_i, [_p] * 7 + [_sz] + [_i] * 7 + [_f, _i, _p]),
     "gqa_decode_balanced_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "gqa_decode_paged_fp8": (_i, [_p, _p, _p, _f, _f, _p, _p, _p, _p, _sz] + [_i] * 7 + [_f, _i, _p]),
     "gqa_prefill_causal": (_i, [_p] * 7 + [_i] * 8 + [_f, _i, _p]),
     "gqa_prefill_paged": (_i, [_p] * 9 + [_i] * 8 + [_f, _i, _p]),
     "gqa_combine_splits": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "gqa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "gqa_status_string": (ctypes.c_char_p, [_i]),
     "gqa_validate_decode": (_i, [_p] * 8 + [_i] * 8 + [_f, _i]),
+    "gqa_validate_decode_fp8": (_i, [_p, _p, _p, _f, _f, _p, _p, _p] + [_i] * 7 + [_f, _i]),
     "gqa_validate_prefill": (_i, [_p] * 7 + [_i] * 8 + [_f, _i]),
     "gqa_validate_prefill_paged": (_i, [_p] * 9 + [_i] * 8 + [_f, _i]),
     "gqa_validate_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _i]),
@@ -200,6 +203,43 @@ def combine_splits(ws_o, ws_lse, out_dtype=torch.bfloat16, out=None):
     st = lib.gqa_combine_splits(_ptr(ws_o), _ptr(ws_lse), _ptr(out), B, Hq, D, ns,
                                 _DTYPE_CODE[out.dtype], _stream(ws_o.device))
     _check(st, "gqa_combine_splits")
+    return out
+
+
+def decode_paged_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, page_table,
+                     context_lens, fmt: str = "e4m3", scale: float | None = None, out=None,
+                     workspace=None):
+    """Paged GQA decode over an 8-bit KV pool (uint8 bytes in format ``fmt``, "e4m3" or
+    "e5m2"; element value = scale * fp8(byte)); q and out bf16; returns out [B][Hq][D]."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.uint8, 4)
+    _need(v_cache, "v_cache", torch.uint8, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    if fmt not in _FP8_CODE:
+        raise ValueError(f"unknown 8-bit format {fmt}")
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes do not match q")
+    if page_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("page_table / context_lens batch mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+    if workspace is None:
+        workspace = balanced_workspace(B, Hq, Hkv, D, q.device)
+    _need(workspace, "workspace")
+    st = lib.gqa_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale),
+                                  float(v_scale), _ptr(page_table), _ptr(context_lens), _ptr(out),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  B, Hq, Hkv, D, P, page_table.shape[1], num_pages, scale,
+                                  _FP8_CODE[fmt], _stream(q.device))
+    _check(st, "gqa_decode_paged_fp8")
     return out
 
 

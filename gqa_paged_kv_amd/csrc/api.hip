@@ -17,6 +17,10 @@ int launch_gather(const void* cache, const int32_t* pt, const int32_t* lens, voi
 int launch_decode_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
                            const int32_t* lens, void* out, void* slots, int B, int Hq, int Hkv,
                            int D, int max_pages, float scale, int dtype, hipStream_t s);
+int launch_decode_balanced_fp8(const void* q, const void* k, const void* v, float k_scale,
+                               float v_scale, const int32_t* pt, const int32_t* lens, void* out,
+                               void* ws, int B, int Hq, int Hkv, int D, int max_pages,
+                               float scale, int kv_dtype, hipStream_t s);
 int launch_prefill(const void* q, const void* k, const void* v, void* out, void* k_cache,
                    void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s);
@@ -70,6 +74,22 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
                                 B, Hq, Hkv, D, max_pages, ns, scale, dtype, s);
   if (st != GQA_OK) return st;
   return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, ns, dtype, s);
+}
+
+int gqa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                         float v_scale, const int32_t* page_table, const int32_t* context_lens,
+                         void* out, void* workspace, size_t workspace_bytes, int B, int Hq,
+                         int Hkv, int D, int P, int max_pages, int num_pages, float scale,
+                         int kv_dtype, void* stream) {
+  int st = gqa_validate_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, page_table,
+                                   context_lens, out, B, Hq, Hkv, D, P, max_pages, num_pages,
+                                   scale, kv_dtype);
+  if (st != GQA_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
+  if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
+  return gqa::launch_decode_balanced_fp8(q, k_cache, v_cache, k_scale, v_scale, page_table,
+                                         context_lens, out, workspace, B, Hq, Hkv, D, max_pages,
+                                         scale, kv_dtype, (hipStream_t)stream);
 }
 
 int gqa_combine_splits(const float* ws_o, const float* ws_lse, void* out, int B, int Hq, int D,

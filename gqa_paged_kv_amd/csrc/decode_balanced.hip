@@ -82,13 +82,15 @@ __device__ __forceinline__ long items_before(const int32_t* __restrict__ context
   return (long)Hkv * wave_sum(part);
 }
 
-template <typename T, int D, int G>
+// T: q / out element type; TKV: cache element type (T, or an 8-bit float whose per-tensor
+// scales are folded in: k_scale into scale_log2, v_scale into out_scale).
+template <typename T, int D, int G, typename TKV = T>
 __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
+    const T* __restrict__ q, const TKV* __restrict__ k_cache, const TKV* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ context_lens,
     T* __restrict__ out, float* __restrict__ slots, int B, int Hq, int Hkv, int max_pages,
-    float scale_log2) {
-  using S = DecodeShape<T, D, G>;
+    float scale_log2, float out_scale) {
+  using S = DecodeShape<TKV, D, G>;
   static_assert(S::HG == 1, "all heads of the group in one wave");
   constexpr int W32 = S::W32;
   constexpr int E = S::E;
@@ -143,12 +145,12 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     const char* vp = (const char*)v_cache + off;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      load_row<T, D>(kp + i * 4 * S::ROW, qd, kb[buf][i]);
-      load_row<T, D>(vp + i * 4 * S::ROW, qd, vb[buf][i]);
+      load_row<TKV, D>(kp + i * 4 * S::ROW, qd, kb[buf][i]);
+      load_row<TKV, D>(vp + i * 4 * S::ROW, qd, vb[buf][i]);
     }
   };
 
-  WaveState<T, D, G> st;
+  WaveState<T, D, G, TKV> st;
   long seg_start = lo;  // first item of the current segment
   st.init(q + ((size_t)b * Hq + kvh * G) * D, qd, scale_log2 < 0.f);
   int T_b = min(context_lens[b], max_pages * kPage);
@@ -175,14 +177,14 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     if (seg_start == first && pg + 1 == np) {
 #pragma unroll
       for (int hw = 0; hw < G; ++hw)
-        store_row(out + ((size_t)b * Hq + kvh * G + hw) * D, hw, 1.0f / st.l[hw]);
+        store_row(out + ((size_t)b * Hq + kvh * G + hw) * D, hw, out_scale / st.l[hw]);
       return;
     }
     const int slot = seg_start == lo ? 0 : 1;
     float* base = slots + ((size_t)gw * 2 + slot) * SLOT;
 #pragma unroll
     for (int hw = 0; hw < G; ++hw) {
-      const float inv = 1.0f / st.l[hw];
+      const float inv = out_scale / st.l[hw];
       if (r == 0) {
 #pragma unroll
         for (int e = 0; e < E; ++e) base[hw * (D + 1) + lane_dim<T, D>(qd, e)] = st.acc[hw][e] * inv;
@@ -339,10 +341,11 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
 
 // ---- host side --------------------------------------------------------------------------
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, typename TKV = T>
 static int launch_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
                            const int32_t* lens, void* out, void* slots_ws, int B, int Hq,
-                           int Hkv, int max_pages, float scale, hipStream_t s) {
+                           int Hkv, int max_pages, float scale, hipStream_t s,
+                           float out_scale = 1.0f) {
   // Persistent grid = resident workgroups; a per-device cache of an occupancy query
   // (every thread computes and stores the same value).
   static int grid_cache[64] = {0};
@@ -353,7 +356,7 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return GQA_ERR_LAUNCH;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel<T, D, G>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel<T, D, G, TKV>,
                                                      kDecodeThreads, 0) != hipSuccess)
       return GQA_ERR_LAUNCH;
     grid = cus * (per_cu > 0 ? per_cu : 1);
@@ -361,9 +364,9 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
     grid_cache[dev] = grid;
   }
   float* slots = (float*)slots_ws;
-  hipLaunchKernelGGL((balanced_kernel<T, D, G>), dim3(grid), dim3(kDecodeThreads), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, pt, lens, (T*)out, slots, B, Hq, Hkv,
-                     max_pages, scale * kLog2e);
+  hipLaunchKernelGGL((balanced_kernel<T, D, G, TKV>), dim3(grid), dim3(kDecodeThreads), 0, s,
+                     (const T*)q, (const TKV*)k, (const TKV*)v, pt, lens, (T*)out, slots, B, Hq,
+                     Hkv, max_pages, scale * kLog2e, out_scale);
   const unsigned fix_grid = (unsigned)(((long)B * Hkv + kFixupWaves - 1) / kFixupWaves);
   hipLaunchKernelGGL((fixup_kernel<T, D, G>), dim3(fix_grid), dim3(kFixupWaves * kWave), 0, s,
                      slots, lens, (T*)out, B, Hq, Hkv, max_pages, grid * kDecodeWaves);
@@ -394,6 +397,37 @@ int launch_decode_balanced(const void* q, const void* k, const void* v, const in
     if (D == 128) return balanced_group<float, 128>(G, q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
     if (D == 64) return balanced_group<float, 64>(G, q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
   }
+  return GQA_ERR_UNSUPPORTED;
+}
+
+// 8-bit cache: bf16 q / out, D = 128, G <= 8. k_scale is folded into the score scale and
+// v_scale into the output normalisation.
+template <typename TKV>
+static int balanced_group_fp8(int G, const void* q, const void* k, const void* v,
+                              const int32_t* pt, const int32_t* lens, void* out, void* ws, int B,
+                              int Hq, int Hkv, int max_pages, float scale, float v_scale,
+                              hipStream_t s) {
+  switch (G) {
+    case 1: return launch_balanced<bf16_t, 128, 1, TKV>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, v_scale);
+    case 2: return launch_balanced<bf16_t, 128, 2, TKV>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, v_scale);
+    case 4: return launch_balanced<bf16_t, 128, 4, TKV>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, v_scale);
+    case 8: return launch_balanced<bf16_t, 128, 8, TKV>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, v_scale);
+    default: return GQA_ERR_UNSUPPORTED;
+  }
+}
+
+int launch_decode_balanced_fp8(const void* q, const void* k, const void* v, float k_scale,
+                               float v_scale, const int32_t* pt, const int32_t* lens, void* out,
+                               void* ws, int B, int Hq, int Hkv, int D, int max_pages,
+                               float scale, int kv_dtype, hipStream_t s) {
+  if (D != 128) return GQA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (kv_dtype == GQA_FP8_E4M3)
+    return balanced_group_fp8<fp8e4m3_t>(G, q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages,
+                                         scale * k_scale, v_scale, s);
+  if (kv_dtype == GQA_FP8_E5M2)
+    return balanced_group_fp8<fp8e5m2_t>(G, q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages,
+                                         scale * k_scale, v_scale, s);
   return GQA_ERR_UNSUPPORTED;
 }
 

@@ -86,12 +86,16 @@ __device__ __forceinline__ void load_row(const char* row, int qd, uint32_t (&w)[
 }
 
 // Online-softmax state of one wave: HW query heads x (this lane's E dims), one state per
-// DPP row (the row's 16 lanes hold identical m and l).
-template <typename T, int D, int HW>
+// DPP row (the row's 16 lanes hold identical m and l). T: q / output element type; TKV:
+// cache element type (T itself, or an 8-bit float with bf16 q).
+template <typename T, int D, int HW, typename TKV = T>
 struct WaveState {
   static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr bool kFp8 = is_fp8<TKV>();
+  static_assert(!kFp8 || kBf16, "8-bit caches are read with bf16 queries");
   static constexpr int E = D / 16;
   static constexpr int W32 = E * (int)sizeof(T) / 4;
+  static constexpr int WKV = E * (int)sizeof(TKV) / 4;  // cache words per lane per row
   uint32_t qw[HW][W32];
   float m[HW], l[HW], acc[HW][E];
 
@@ -148,15 +152,26 @@ struct WaveState {
   // Consume one page: this lane holds rows kw[i], vw[i] of tokens tok0 + 4*i (i < 4).
   // MASKED: tokens >= t_end are dead (their slots may hold anything, NaN included).
   template <bool MASKED>
-  __device__ __forceinline__ void page(const uint32_t (&kw)[4][W32], uint32_t (&vw)[4][W32],
+  __device__ __forceinline__ void page(const uint32_t (&kw)[4][WKV], uint32_t (&vw)[4][WKV],
                                        int tok0, int t_end, float scale_log2) {
     float s[4][HW];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      uint32_t kb16[kFp8 ? W32 : 1];  // an 8-bit K row widened to bf16 pairs (exact)
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int x = 0; x < WKV; ++x) {
+          kb16[2 * x] = fp8x2_to_bf16x2<TKV>(kw[i][x], false);
+          kb16[2 * x + 1] = fp8x2_to_bf16x2<TKV>(kw[i][x], true);
+        }
+      }
 #pragma unroll
       for (int hw = 0; hw < HW; ++hw) {
         float part = 0.f;
-        if constexpr (kBf16) {
+        if constexpr (kFp8) {
+#pragma unroll
+          for (int x = 0; x < W32; ++x) part = dot2_bf16(qw[hw][x], kb16[x], part);
+        } else if constexpr (kBf16) {
 #pragma unroll
           for (int x = 0; x < W32; ++x) part = dot2_bf16(qw[hw][x], kw[i][x], part);
         } else {
@@ -175,7 +190,7 @@ struct WaveState {
 #pragma unroll
         for (int hw = 0; hw < HW; ++hw) s[i][hw] = -INFINITY;
 #pragma unroll
-        for (int x = 0; x < W32; ++x) vw[i][x] = 0u;  // never multiply a dead slot
+        for (int x = 0; x < WKV; ++x) vw[i][x] = 0u;  // never multiply a dead slot
       }
     }
     // The reference max m is raised lazily, only when a new score exceeds it by more
@@ -210,7 +225,13 @@ struct WaveState {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float vf[E];
-      if constexpr (kBf16) {
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int x = 0; x < WKV; ++x) {
+          fp8x2_to_f32<TKV>(vw[i][x], false, vf[4 * x], vf[4 * x + 1]);
+          fp8x2_to_f32<TKV>(vw[i][x], true, vf[4 * x + 2], vf[4 * x + 3]);
+        }
+      } else if constexpr (kBf16) {
 #pragma unroll
         for (int x = 0; x < W32; ++x) {
           vf[2 * x] = bf16lo_to_f32(vw[i][x]);

@@ -1,6 +1,8 @@
 // Device helpers shared by the libgqa kernels (gfx950 / CDNA4, wave64).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -14,6 +16,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct bf16_t {
   uint16_t bits;
 };
+
+// 8-bit floating-point cache elements (raw bytes): E4M3 (bias 7, no infinities) and E5M2
+// (bias 15, IEEE-style specials). gfx950 converts both natively.
+struct fp8e4m3_t {
+  uint8_t bits;
+};
+struct fp8e5m2_t {
+  uint8_t bits;
+};
+template <typename T>
+constexpr bool is_fp8() {
+  return sizeof(T) == 1;
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -35,6 +50,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Bytes 2*hi, 2*hi+1 of a word of 8-bit floats -> two floats / one packed bf16 pair (exact:
+// every E4M3 and E5M2 value is a bf16 value). The conversion is the hardware's
+// (v_cvt_pk_f32_fp8 / _bf8, v_cvt_scalef32_pk_bf16_fp8 / _bf8 with scale 1).
+template <typename T>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, bool hi, float& a, float& b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 v;
+  if constexpr (std::is_same<T, fp8e4m3_t>::value)
+    v = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  else
+    v = hi ? __builtin_amdgcn_cvt_pk_f32_bf8(w, true) : __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+  a = v[0];
+  b = v[1];
+}
+template <typename T>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  bf16x2_t v;
+  if constexpr (std::is_same<T, fp8e4m3_t>::value)
+    v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  else
+    v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
   return __builtin_bit_cast(uint32_t, v);
 }
 

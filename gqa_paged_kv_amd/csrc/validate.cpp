@@ -112,6 +112,22 @@ int gqa_validate_prefill(const void* q, const void* k, const void* v, const void
   return GQA_OK;
 }
 
+int gqa_validate_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                            float k_scale, float v_scale, const int32_t* page_table,
+                            const int32_t* context_lens, const void* out, int B, int Hq, int Hkv,
+                            int D, int P, int max_pages, int num_pages, float scale,
+                            int kv_dtype) {
+  if (kv_dtype != GQA_FP8_E4M3 && kv_dtype != GQA_FP8_E5M2) return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f)
+    return GQA_ERR_INVALID_ARG;
+  int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
+                               nullptr, B, Hq, Hkv, D, P, max_pages, num_pages, 1, scale,
+                               GQA_BF16);
+  if (st != GQA_OK) return st;
+  if (D != 128 || Hq / Hkv > 8) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
 int gqa_validate_prefill_paged(const void* q, const void* k, const void* v, const void* k_cache,
                                const void* v_cache, const int32_t* page_table,
                                const int32_t* past_lens, const int32_t* new_lens, const void* out,

@@ -54,7 +54,12 @@ typedef enum {
   GQA_ERR_LAUNCH = 3       /* the HIP runtime refused the kernel launch */
 } gqa_status;
 
-typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+typedef enum {
+  GQA_F32 = 0,
+  GQA_BF16 = 1,
+  GQA_FP8_E4M3 = 2, /* 8-bit float, 4 exponent bits (bias 7), 3 mantissa bits, no inf; cache only */
+  GQA_FP8_E5M2 = 3  /* 8-bit float, 5 exponent bits (bias 15), 2 mantissa bits; cache only */
+} gqa_dtype;
 
 /*
  * Single-token decode over a paged cache, optionally split along the context
@@ -111,6 +116,30 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
                               void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                               int D, int P, int max_pages, int num_pages, float scale, int dtype,
                               void* stream);
+
+/*
+ * Decode over an 8-bit floating-point KV pool (the pages quote FP8 KV caches as the next
+ * halving of decode bytes: page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", the
+ * performance discussion after section "核心参数调优：PackGQA与NumSplits的协同舞蹈"; page
+ * "TensorRT对Grouped Query Attention的支持进展", section "显存带宽瓶颈下的理性妥协"). Same
+ * result and partition as gqa_decode_paged_balanced with every cache byte x read as
+ * k_scale * fp8(x) (K) or v_scale * fp8(x) (V); products and sums in fp32.
+ *
+ *   q            [B][Hq][D]              bf16
+ *   k_cache,     [num_pages][Hkv][P][D]  one byte per element, format kv_dtype
+ *   v_cache                              (GQA_FP8_E4M3 or GQA_FP8_E5M2)
+ *   k_scale,     per-tensor scales, finite and > 0
+ *   v_scale
+ *   out          [B][Hq][D]              bf16 (round to nearest even)
+ *   workspace    as for gqa_decode_paged_balanced (same size function)
+ *   other arguments as for gqa_decode_paged_balanced.
+ * Supported: D = 128, G in {1, 2, 4, 8}, P = 16. Enqueues two kernels (decode + fix-up).
+ */
+int gqa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                         float v_scale, const int32_t* page_table, const int32_t* context_lens,
+                         void* out, void* workspace, size_t workspace_bytes, int B, int Hq,
+                         int Hkv, int D, int P, int max_pages, int num_pages, float scale,
+                         int kv_dtype, void* stream);
 
 /*
  * Causal prefill of S new tokens per sequence, with the new K/V appended to
@@ -184,6 +213,11 @@ int gqa_validate_prefill(const void* q, const void* k, const void* v, const void
                          const void* v_cache, const int32_t* page_table, const void* out, int B,
                          int S, int Hq, int Hkv, int D, int P, int max_pages, int num_pages,
                          float scale, int dtype);
+int gqa_validate_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                            float k_scale, float v_scale, const int32_t* page_table,
+                            const int32_t* context_lens, const void* out, int B, int Hq, int Hkv,
+                            int D, int P, int max_pages, int num_pages, float scale,
+                            int kv_dtype);
 int gqa_validate_prefill_paged(const void* q, const void* k, const void* v, const void* k_cache,
                                const void* v_cache, const int32_t* page_table,
                                const int32_t* past_lens, const int32_t* new_lens, const void* out,

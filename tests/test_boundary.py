@@ -139,6 +139,23 @@ def test_chunked_prefill_validation_rules(lib):
     assert _vpp(lib, P=32) == g.ERR_UNSUPPORTED
 
 
+def test_fp8_decode_validation_rules(lib):
+    v = lib.gqa_validate_decode_fp8
+    args = lambda **kw: dict(dict(q=FAKE, k=FAKE, vv=FAKE, ks=0.01, vs=0.02, pt=FAKE, lens=FAKE,
+                                  out=FAKE, B=4, Hq=32, Hkv=8, D=128, P=16, mp=64, npg=4096,
+                                  scale=0.088, dt=g.FP8_E4M3), **kw)
+    call = lambda a: v(a["q"], a["k"], a["vv"], a["ks"], a["vs"], a["pt"], a["lens"], a["out"],
+                       a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["mp"], a["npg"], a["scale"],
+                       a["dt"])
+    assert call(args()) == g.OK
+    assert call(args(dt=g.FP8_E5M2)) == g.OK
+    for bad in (dict(dt=g.BF16), dict(dt=7), dict(ks=0.0), dict(vs=-1.0), dict(ks=float("inf")),
+                dict(k=None), dict(lens=None), dict(Hq=30)):
+        assert call(args(**bad)) == g.ERR_INVALID_ARG, bad
+    assert call(args(D=64)) == g.ERR_UNSUPPORTED
+    assert call(args(Hq=32, Hkv=2)) == g.ERR_UNSUPPORTED  # G = 16: not built for 8-bit caches
+
+
 def test_combine_validation_rules(lib):
     v = lib.gqa_validate_combine
     assert v(FAKE, FAKE, FAKE, 4, 32, 128, 8, g.BF16) == g.OK
@@ -158,6 +175,9 @@ def test_entry_points_reject_before_enqueueing(lib):
     assert st == g.ERR_UNSUPPORTED
     st = lib.gqa_prefill_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 64, 8,
                                2, 128, 16, 4, 8, 0.1, g.BF16, None)
+    assert st == g.ERR_INVALID_ARG
+    st = lib.gqa_decode_paged_fp8(FAKE, FAKE, FAKE, 0.0, 1.0, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2,
+                                  8, 2, 128, 16, 4, 8, 0.1, g.FP8_E4M3, None)
     assert st == g.ERR_INVALID_ARG
     st = lib.gqa_combine_splits(FAKE, None, FAKE, 1, 8, 128, 2, g.BF16, None)
     assert st == g.ERR_INVALID_ARG
