@@ -327,3 +327,45 @@ def test_decode_scale_sign_and_magnitude(gpu_lib, scale, path):
     else:
         out = _run_bal(gpu_lib, x)
     assert_close(out, _ref(x), "bf16", f"decode scale={scale} {path}")
+
+
+# ---------------------------------------------------------------- shared-prefix pages
+
+def _shared_prefix_inputs(dtype, hq, hkv, prefix, tails, seed):
+    """Beams / sequences that share the physical pages of a common prefix: sequence b's page
+    table starts with the same ceil(prefix/P)... pages (the prefix must end on a page
+    boundary to be shareable), then private pages for its own tail."""
+    P = 16
+    assert prefix % P == 0
+    lens = [prefix + t for t in tails]
+    x = synth.decode_inputs(len(tails), hq, hkv, 128, P, lens, dtype, seed=seed, poison=False)
+    pt = x.page_table.clone()
+    npre = prefix // P
+    pt[:, :npre] = pt[0, :npre]  # every sequence reads sequence 0's prefix pages
+    x.page_table = pt
+    return x
+
+
+@pytest.mark.parametrize("path", ["split1", "split4", "balanced"])
+@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 32, 8), ("f32", 8, 2), ("bf16", 32, 2)])
+def test_shared_prefix_pages(gpu_lib, path, dtype, hq, hkv):
+    """Page-table aliasing: 5 sequences share a 160-token prefix and differ after it. The
+    kernels only read the pool, so aliased pages must give exactly the oracle's result."""
+    print(f"[decode] shared prefix {path} {dtype} {hq}x{hkv}", flush=True)
+    x = _shared_prefix_inputs(dtype, hq, hkv, 160, [0, 1, 15, 16, 300], seed=71).to(DEV)
+    out = _run(gpu_lib, x, ns=int(path[-1])) if path.startswith("split") else _run_bal(gpu_lib, x)
+    assert_close(out, _ref(x), dtype, f"shared prefix {path}")
+    # sequence 0 holds exactly the prefix: every other sequence's prefix part is its prefix
+    assert int(x.context_lens[0]) == 160
+
+
+def test_shared_prefix_identical_sequences_give_identical_rows(gpu_lib):
+    """Two sequences with the same page-table row, length and query give bit-identical rows."""
+    print("[decode] shared prefix identical", flush=True)
+    x = synth.decode_inputs(3, 32, 8, 128, 16, [500, 777, 500], "bf16", seed=72, poison=False)
+    x.page_table[2] = x.page_table[0]
+    x.q[2] = x.q[0]
+    x = x.to(DEV)
+    out = _run_bal(gpu_lib, x)
+    assert torch.equal(out[0], out[2])
+    assert_close(out, _ref(x), "bf16", "identical beams")
