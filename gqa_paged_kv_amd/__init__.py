@@ -29,6 +29,7 @@ SIGNATURES = {
     "gqa_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _p, _p] + [_i] * 8 + [_f, _i, _p]),
     "gqa_decode_paged_balanced": (_i, [_p] * 7 + [_sz] + [_i] * 7 + [_f, _i, _p]),
     "gqa_decode_balanced_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "gqa_decode_append": (_i, [_p] * 9 + [_sz] + [_i] * 7 + [_f, _i, _p]),
     "gqa_decode_paged_fp8": (_i, [_p, _p, _p, _f, _f, _p, _p, _p, _p, _sz] + [_i] * 7 + [_f, _i, _p]),
     "gqa_prefill_causal": (_i, [_p] * 7 + [_i] * 8 + [_f, _i, _p]),
     "gqa_prefill_paged": (_i, [_p] * 9 + [_i] * 8 + [_f, _i, _p]),
@@ -203,6 +204,43 @@ def combine_splits(ws_o, ws_lse, out_dtype=torch.bfloat16, out=None):
     st = lib.gqa_combine_splits(_ptr(ws_o), _ptr(ws_lse), _ptr(out), B, Hq, D, ns,
                                 _DTYPE_CODE[out.dtype], _stream(ws_o.device))
     _check(st, "gqa_combine_splits")
+    return out
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, page_table, context_lens,
+                  scale: float | None = None, out=None, workspace=None):
+    """One decode step with its own token: k_new / v_new [B][Hkv][D] are written at position
+    context_lens[b] of each sequence, which then attends context_lens[b] + 1 tokens (the new
+    one included). context_lens is not changed. Returns out [B][Hq][D]."""
+    lib = load()
+    _need(q, "q", dim=3)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _need(k_new, "k_new", q.dtype, 3)
+    _need(v_new, "v_new", q.dtype, 3)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape or k_new.shape != (B, Hkv, D) or \
+            v_new.shape != k_new.shape:
+        raise ValueError("shapes do not match")
+    if page_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("page_table / context_lens batch mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = balanced_workspace(B, Hq, Hkv, D, q.device)
+    st = lib.gqa_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(page_table), _ptr(context_lens), _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), B, Hq, Hkv, D, P,
+                               page_table.shape[1], num_pages, scale, _DTYPE_CODE[q.dtype],
+                               _stream(q.device))
+    _check(st, "gqa_decode_append")
     return out
 
 

@@ -17,6 +17,10 @@ int launch_gather(const void* cache, const int32_t* pt, const int32_t* lens, voi
 int launch_decode_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
                            const int32_t* lens, void* out, void* slots, int B, int Hq, int Hkv,
                            int D, int max_pages, float scale, int dtype, hipStream_t s);
+int launch_decode_append(const void* q, const void* k_new, const void* v_new, void* k, void* v,
+                         const int32_t* pt, const int32_t* lens, void* out, void* ws, int B,
+                         int Hq, int Hkv, int D, int max_pages, float scale, int dtype,
+                         hipStream_t s);
 int launch_decode_balanced_fp8(const void* q, const void* k, const void* v, float k_scale,
                                float v_scale, const int32_t* pt, const int32_t* lens, void* out,
                                void* ws, int B, int Hq, int Hkv, int D, int max_pages,
@@ -74,6 +78,23 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
                                 B, Hq, Hkv, D, max_pages, ns, scale, dtype, s);
   if (st != GQA_OK) return st;
   return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, ns, dtype, s);
+}
+
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, const int32_t* page_table, const int32_t* context_lens,
+                      void* out, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                      int D, int P, int max_pages, int num_pages, float scale, int dtype,
+                      void* stream) {
+  if (!k_new || !v_new) return GQA_ERR_INVALID_ARG;
+  int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
+                               nullptr, B, Hq, Hkv, D, P, max_pages, num_pages, 1, scale, dtype);
+  if (st != GQA_OK) return st;
+  if (Hq / Hkv > 8) return GQA_ERR_UNSUPPORTED;
+  if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
+  if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
+  return gqa::launch_decode_append(q, k_new, v_new, k_cache, v_cache, page_table, context_lens,
+                                   out, workspace, B, Hq, Hkv, D, max_pages, scale, dtype,
+                                   (hipStream_t)stream);
 }
 
 int gqa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,

@@ -31,11 +31,19 @@ constexpr int kBalancedMaxWaves = 4096;  // upper bound of the persistent grid (
 
 // Workspace data region: kBalancedMaxWaves x 2 partial slots of G x (D + 1) floats.
 
-__device__ __forceinline__ int pages_of(const int32_t* __restrict__ context_lens, int b,
-                                        int max_pages) {
+// Tokens attended by sequence b: T_b clamped to [0, max_pages * P]; with append = 1 (the
+// step's own token is appended at position T_b first) T_b is clamped to
+// [0, max_pages * P - 1] and one is added.
+__device__ __forceinline__ int seq_len(const int32_t* __restrict__ context_lens, int b,
+                                       int max_pages, int append) {
+  const int cap = max_pages * kPage - append;
   int T = context_lens[b];
-  T = T < 0 ? 0 : (T > max_pages * kPage ? max_pages * kPage : T);
-  return (T + kPage - 1) / kPage;
+  T = T < 0 ? 0 : (T > cap ? cap : T);
+  return T + append;
+}
+__device__ __forceinline__ int pages_of(const int32_t* __restrict__ context_lens, int b,
+                                        int max_pages, int append) {
+  return (seq_len(context_lens, b, max_pages, append) + kPage - 1) / kPage;
 }
 
 __device__ __forceinline__ long wave_sum(long x) {
@@ -52,11 +60,11 @@ __device__ __forceinline__ int share_owner(long N, long x, int nw) {
 // First sequence b whose items end past item x (so np_b > 0), with np_b and the index of
 // its first item: wave-wide inclusive scans of ceil(T_b / P), 64 sequences per step.
 __device__ __forceinline__ void locate_item(const int32_t* __restrict__ context_lens, int B,
-                                            int Hkv, int max_pages, long x, int lane, int& b,
-                                            int& np, long& seq_base) {
+                                            int Hkv, int max_pages, int append, long x, int lane,
+                                            int& b, int& np, long& seq_base) {
   long base = 0;
   for (int c = 0; c < B; c += kWave) {
-    const int n = c + lane < B ? pages_of(context_lens, c + lane, max_pages) : 0;
+    const int n = c + lane < B ? pages_of(context_lens, c + lane, max_pages, append) : 0;
     int incl = n;
     for (int off = 1; off < kWave; off <<= 1) {
       const int v = __shfl_up(incl, off);
@@ -76,21 +84,23 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ context_
 
 // Index of the first item of sequence b (exclusive scan up to b).
 __device__ __forceinline__ long items_before(const int32_t* __restrict__ context_lens, int b,
-                                             int Hkv, int max_pages, int lane) {
+                                             int Hkv, int max_pages, int append, int lane) {
   long part = 0;
-  for (int bb = lane; bb < b; bb += kWave) part += pages_of(context_lens, bb, max_pages);
+  for (int bb = lane; bb < b; bb += kWave) part += pages_of(context_lens, bb, max_pages, append);
   return (long)Hkv * wave_sum(part);
 }
 
 // T: q / out element type; TKV: cache element type (T, or an 8-bit float whose per-tensor
 // scales are folded in: k_scale into scale_log2, v_scale into out_scale).
-template <typename T, int D, int G, typename TKV = T>
+template <typename T, int D, int G, typename TKV = T, bool APPEND = false>
 __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     const T* __restrict__ q, const TKV* __restrict__ k_cache, const TKV* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ context_lens,
     T* __restrict__ out, float* __restrict__ slots, int B, int Hq, int Hkv, int max_pages,
-    float scale_log2, float out_scale) {
+    float scale_log2, float out_scale, const TKV* __restrict__ k_new,
+    const TKV* __restrict__ v_new, TKV* __restrict__ k_store, TKV* __restrict__ v_store) {
   using S = DecodeShape<TKV, D, G>;
+  constexpr int append = APPEND ? 1 : 0;
   static_assert(S::HG == 1, "all heads of the group in one wave");
   constexpr int W32 = S::W32;
   constexpr int E = S::E;
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
 
   // ---- total item count N = Hkv * sum_b ceil(T_b / P) ----
   long part = 0;
-  for (int bb = lane; bb < B; bb += kWave) part += pages_of(context_lens, bb, max_pages);
+  for (int bb = lane; bb < B; bb += kWave) part += pages_of(context_lens, bb, max_pages, append);
   const long N = (long)Hkv * wave_sum(part);
 
   if (N == 0) return;
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   // ---- locate the sequence holding item lo ----
   int b = 0, np = 1;
   long seq_base = 0;  // first item of sequence b
-  locate_item(context_lens, B, Hkv, max_pages, lo, lane, b, np, seq_base);
+  locate_item(context_lens, B, Hkv, max_pages, append, lo, lane, b, np, seq_base);
   const long rem = lo - seq_base;
   int kvh = (int)(rem / np);
   int pg = (int)(rem % np);
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
         int n = 0;
         do {
           ++cb;
-          n = cb < B ? pages_of(context_lens, cb, max_pages) : 1;
+          n = cb < B ? pages_of(context_lens, cb, max_pages, append) : 1;
         } while (n == 0);
         cnp = n;
       }
@@ -138,22 +148,31 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   };
 
   uint32_t kb[3][4][W32], vb[3][4][W32];
+  // append: the row of the step's own token (slot (L - 1) % P of the sequence's last page)
+  // is read from k_new / v_new instead of the pool (the pool gets it in consume()).
   auto load_page = [&](int buf, int cb, int ckv, int cpg) {
     const size_t off = (size_t)page_table[(size_t)cb * max_pages + cpg] * page_stride +
                        (size_t)ckv * S::PAGE + r * S::ROW;
     const char* kp = (const char*)k_cache + off;
     const char* vp = (const char*)v_cache + off;
+    int new_row = -1;
+    if constexpr (APPEND) {
+      const int L = seq_len(context_lens, cb, max_pages, 1);
+      if (cpg == (L - 1) / kPage) new_row = (L - 1) % kPage;
+    }
+    const size_t new_off = ((size_t)cb * Hkv + ckv) * S::ROW;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      load_row<TKV, D>(kp + i * 4 * S::ROW, qd, kb[buf][i]);
-      load_row<TKV, D>(vp + i * 4 * S::ROW, qd, vb[buf][i]);
+      const bool nr = 4 * i + r == new_row;
+      load_row<TKV, D>(nr ? (const char*)k_new + new_off : kp + i * 4 * S::ROW, qd, kb[buf][i]);
+      load_row<TKV, D>(nr ? (const char*)v_new + new_off : vp + i * 4 * S::ROW, qd, vb[buf][i]);
     }
   };
 
   WaveState<T, D, G, TKV> st;
   long seg_start = lo;  // first item of the current segment
   st.init(q + ((size_t)b * Hq + kvh * G) * D, qd, scale_log2 < 0.f);
-  int T_b = min(context_lens[b], max_pages * kPage);
+  int T_b = seq_len(context_lens, b, max_pages, append);
 
   auto store_row = [&](T* dst, int hw, float inv) {
     if (r == 0) {
@@ -197,6 +216,18 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   // when the next item starts a new unit.
   auto consume = [&](int buf, long i) {
     const int tok0 = pg * kPage + r;
+    if (APPEND && pg + 1 == np) {  // write the step's token into its pool slot (once)
+      const int slot = (T_b - 1) % kPage;
+      const size_t off = (size_t)page_table[(size_t)b * max_pages + pg] * page_stride +
+                         (size_t)kvh * S::PAGE + (size_t)slot * S::ROW;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        if (4 * ii + r == slot) {
+          store_kv_row<TKV, D>((char*)k_store + off, qd, kb[buf][ii]);
+          store_kv_row<TKV, D>((char*)v_store + off, qd, vb[buf][ii]);
+        }
+      }
+    }
     if (pg + 1 < np) {
       st.template page<false>(kb[buf], vb[buf], tok0, T_b, abs_scale(scale_log2));
     } else {
@@ -208,7 +239,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     if (unit_end && i + 1 < hi) {
       seg_start = i + 1;
       st.init(q + ((size_t)b * Hq + kvh * G) * D, qd, scale_log2 < 0.f);
-      T_b = min(context_lens[b], max_pages * kPage);
+      T_b = seq_len(context_lens, b, max_pages, append);
     }
   };
 
@@ -244,7 +275,7 @@ constexpr int kFixupWaves = 4;
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
     const float* __restrict__ slots, const int32_t* __restrict__ context_lens,
-    T* __restrict__ out, int B, int Hq, int Hkv, int max_pages, int nw) {
+    T* __restrict__ out, int B, int Hq, int Hkv, int max_pages, int nw, int append) {
   constexpr int SLOT = G * (D + 1);
   constexpr int DL = D / kWave;  // dims per lane
   const int lane = lane_id();
@@ -255,12 +286,12 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
   // N and the first item of sequence b in one pass over the page counts
   long part_all = 0, part_before = 0;
   for (int bb = lane; bb < B; bb += kWave) {
-    const int n = pages_of(context_lens, bb, max_pages);
+    const int n = pages_of(context_lens, bb, max_pages, append);
     part_all += n;
     part_before += bb < b ? n : 0;
   }
   const long N = (long)Hkv * wave_sum(part_all);
-  const int np = pages_of(context_lens, b, max_pages);
+  const int np = pages_of(context_lens, b, max_pages, append);
   T* dst = out + ((size_t)b * Hq + kvh * G) * D;
   if (np == 0) {  // T_b == 0: the output is zero
     for (int i = lane; i < G * D; i += kWave) {
@@ -341,11 +372,13 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
 
 // ---- host side --------------------------------------------------------------------------
 
-template <typename T, int D, int G, typename TKV = T>
+template <typename T, int D, int G, typename TKV = T, bool APPEND = false>
 static int launch_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
                            const int32_t* lens, void* out, void* slots_ws, int B, int Hq,
                            int Hkv, int max_pages, float scale, hipStream_t s,
-                           float out_scale = 1.0f) {
+                           float out_scale = 1.0f, const void* k_new = nullptr,
+                           const void* v_new = nullptr, void* k_store = nullptr,
+                           void* v_store = nullptr) {
   // Persistent grid = resident workgroups; a per-device cache of an occupancy query
   // (every thread computes and stores the same value).
   static int grid_cache[64] = {0};
@@ -356,7 +389,7 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return GQA_ERR_LAUNCH;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel<T, D, G, TKV>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel<T, D, G, TKV, APPEND>,
                                                      kDecodeThreads, 0) != hipSuccess)
       return GQA_ERR_LAUNCH;
     grid = cus * (per_cu > 0 ? per_cu : 1);
@@ -364,12 +397,14 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
     grid_cache[dev] = grid;
   }
   float* slots = (float*)slots_ws;
-  hipLaunchKernelGGL((balanced_kernel<T, D, G, TKV>), dim3(grid), dim3(kDecodeThreads), 0, s,
+  hipLaunchKernelGGL((balanced_kernel<T, D, G, TKV, APPEND>), dim3(grid), dim3(kDecodeThreads), 0, s,
                      (const T*)q, (const TKV*)k, (const TKV*)v, pt, lens, (T*)out, slots, B, Hq,
-                     Hkv, max_pages, scale * kLog2e, out_scale);
+                     Hkv, max_pages, scale * kLog2e, out_scale, (const TKV*)k_new,
+                     (const TKV*)v_new, (TKV*)k_store, (TKV*)v_store);
   const unsigned fix_grid = (unsigned)(((long)B * Hkv + kFixupWaves - 1) / kFixupWaves);
   hipLaunchKernelGGL((fixup_kernel<T, D, G>), dim3(fix_grid), dim3(kFixupWaves * kWave), 0, s,
-                     slots, lens, (T*)out, B, Hq, Hkv, max_pages, grid * kDecodeWaves);
+                     slots, lens, (T*)out, B, Hq, Hkv, max_pages, grid * kDecodeWaves,
+                     APPEND ? 1 : 0);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
@@ -396,6 +431,37 @@ int launch_decode_balanced(const void* q, const void* k, const void* v, const in
   } else {
     if (D == 128) return balanced_group<float, 128>(G, q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
     if (D == 64) return balanced_group<float, 64>(G, q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
+  }
+  return GQA_ERR_UNSUPPORTED;
+}
+
+// Decode with the step's own token appended first (k_new / v_new [B][Hkv][D] go to position
+// T_b of each sequence, which then attends T_b + 1 tokens); G <= 8.
+template <typename T, int D>
+static int balanced_group_append(int G, const void* q, const void* k_new, const void* v_new,
+                                 void* k, void* v, const int32_t* pt, const int32_t* lens,
+                                 void* out, void* ws, int B, int Hq, int Hkv, int max_pages,
+                                 float scale, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_balanced<T, D, 1, T, true>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, 1.0f, k_new, v_new, k, v);
+    case 2: return launch_balanced<T, D, 2, T, true>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, 1.0f, k_new, v_new, k, v);
+    case 4: return launch_balanced<T, D, 4, T, true>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, 1.0f, k_new, v_new, k, v);
+    case 8: return launch_balanced<T, D, 8, T, true>(q, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s, 1.0f, k_new, v_new, k, v);
+    default: return GQA_ERR_UNSUPPORTED;
+  }
+}
+
+int launch_decode_append(const void* q, const void* k_new, const void* v_new, void* k, void* v,
+                         const int32_t* pt, const int32_t* lens, void* out, void* ws, int B,
+                         int Hq, int Hkv, int D, int max_pages, float scale, int dtype,
+                         hipStream_t s) {
+  const int G = Hq / Hkv;
+  if (dtype == GQA_BF16) {
+    if (D == 128) return balanced_group_append<bf16_t, 128>(G, q, k_new, v_new, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
+    if (D == 64) return balanced_group_append<bf16_t, 64>(G, q, k_new, v_new, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
+  } else {
+    if (D == 128) return balanced_group_append<float, 128>(G, q, k_new, v_new, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
+    if (D == 64) return balanced_group_append<float, 64>(G, q, k_new, v_new, k, v, pt, lens, out, ws, B, Hq, Hkv, max_pages, scale, s);
   }
   return GQA_ERR_UNSUPPORTED;
 }

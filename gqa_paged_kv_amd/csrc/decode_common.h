@@ -85,6 +85,20 @@ __device__ __forceinline__ void load_row(const char* row, int qd, uint32_t (&w)[
   }
 }
 
+// Inverse of load_row: write one lane's E elements of a token row.
+template <typename T, int D>
+__device__ __forceinline__ void store_kv_row(char* row, int qd, const uint32_t (&w)[D / 16 * sizeof(T) / 4]) {
+  constexpr int LB = D / 16 * (int)sizeof(T);
+  if constexpr (LB == 8) {
+    *(u32x2_t*)(row + qd * 8) = u32x2_t{w[0], w[1]};
+  } else if constexpr (LB == 16) {
+    *(u32x4_t*)(row + qd * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+  } else {
+    *(u32x4_t*)(row + qd * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+    *(u32x4_t*)(row + D * 2 + qd * 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+  }
+}
+
 // Online-softmax state of one wave: HW query heads x (this lane's E dims), one state per
 // DPP row (the row's 16 lanes hold identical m and l). T: q / output element type; TKV:
 // cache element type (T itself, or an 8-bit float with bf16 q).

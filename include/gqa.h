@@ -118,6 +118,33 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
                               void* stream);
 
 /*
+ * One decode step with its own token appended (the per-step KV append: page "TensorRT对
+ * Grouped Query Attention的支持进展", section "动态形状与KV Cache管理", the cache grows by
+ * one token per generated token). For every sequence b the step's K and V rows
+ * k_new[b][kvh][:], v_new[b][kvh][:] are written at position T_b = context_lens[b]
+ * (slot T_b % P of page page_table[b][T_b / P], bit copies) and
+ * out[b][h] = softmax(scale * q[b][h] . K_b^T) V_b over tokens 0 .. T_b, the new token
+ * included (it is read from k_new / v_new, not back from the pool). The pages holding
+ * positions 0 .. T_b must be in the page table; pages may be shared between sequences
+ * (prefix sharing) except the page that receives the new token. context_lens is not
+ * updated (the caller increments it). T_b is clamped to [0, max_pages * P - 1].
+ *
+ *   q            [B][Hq][D]    dtype
+ *   k_new, v_new [B][Hkv][D]   dtype
+ *   k_cache,     [num_pages][Hkv][P][D] dtype, written only at the new tokens' slots
+ *   v_cache
+ *   out          [B][Hq][D]    dtype
+ *   workspace    as for gqa_decode_paged_balanced
+ * Supported: D in {64, 128}, P = 16, G in {1, 2, 4, 8}, dtype GQA_F32 or GQA_BF16.
+ * Enqueues two kernels (decode with the append folded in + fix-up).
+ */
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, const int32_t* page_table, const int32_t* context_lens,
+                      void* out, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                      int D, int P, int max_pages, int num_pages, float scale, int dtype,
+                      void* stream);
+
+/*
  * Decode over an 8-bit floating-point KV pool (the pages quote FP8 KV caches as the next
  * halving of decode bytes: page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", the
  * performance discussion after section "核心参数调优：PackGQA与NumSplits的协同舞蹈"; page

@@ -179,6 +179,12 @@ def test_entry_points_reject_before_enqueueing(lib):
     st = lib.gqa_decode_paged_fp8(FAKE, FAKE, FAKE, 0.0, 1.0, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2,
                                   8, 2, 128, 16, 4, 8, 0.1, g.FP8_E4M3, None)
     assert st == g.ERR_INVALID_ARG
+    st = lib.gqa_decode_append(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2,
+                               8, 2, 128, 16, 4, 8, 0.1, g.BF16, None)
+    assert st == g.ERR_INVALID_ARG
+    st = lib.gqa_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2,
+                               32, 2, 128, 16, 4, 8, 0.1, g.BF16, None)
+    assert st == g.ERR_UNSUPPORTED  # G = 16
     st = lib.gqa_combine_splits(FAKE, None, FAKE, 1, 8, 128, 2, g.BF16, None)
     assert st == g.ERR_INVALID_ARG
     st = lib.gqa_gather_paged(FAKE, FAKE, FAKE, FAKE, 1, 2, 96, 16, 4, 8, g.BF16, None)
