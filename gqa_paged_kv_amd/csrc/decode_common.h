@@ -236,29 +236,53 @@ struct WaveState {
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[hw][e] *= alpha[hw];
     }
+    if constexpr (kBf16) {
+      // PV on bf16 pairs: this lane holds rows i = 0..3 (tokens tok0 + 4i) of the page, so
+      // for tokens (2j, 2j+1) and each of its dims the two V values are repacked into one
+      // bf16 pair (v_perm_b32) and v_dot2_f32_bf16 adds p_2j v_2j + p_2j+1 v_2j+1 with P
+      // rounded to bf16 (fp32 accumulation; l keeps the unrounded p).
+      uint32_t vb16[4][W32];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vf[E];
-      if constexpr (kFp8) {
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (kFp8) {
 #pragma unroll
-        for (int x = 0; x < WKV; ++x) {
-          fp8x2_to_f32<TKV>(vw[i][x], false, vf[4 * x], vf[4 * x + 1]);
-          fp8x2_to_f32<TKV>(vw[i][x], true, vf[4 * x + 2], vf[4 * x + 3]);
+          for (int x = 0; x < WKV; ++x) {
+            vb16[i][2 * x] = fp8x2_to_bf16x2<TKV>(vw[i][x], false);
+            vb16[i][2 * x + 1] = fp8x2_to_bf16x2<TKV>(vw[i][x], true);
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < W32; ++x) vb16[i][x] = vw[i][x];
         }
-      } else if constexpr (kBf16) {
-#pragma unroll
-        for (int x = 0; x < W32; ++x) {
-          vf[2 * x] = bf16lo_to_f32(vw[i][x]);
-          vf[2 * x + 1] = bf16hi_to_f32(vw[i][x]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) vf[e] = __uint_as_float(vw[i][e]);
       }
 #pragma unroll
-      for (int hw = 0; hw < HW; ++hw)
+      for (int j = 0; j < 2; ++j) {
+        uint32_t pp[HW];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[hw][e] = fmaf(p[i][hw], vf[e], acc[hw][e]);
+        for (int hw = 0; hw < HW; ++hw) pp[hw] = pack_bf16x2(p[2 * j][hw], p[2 * j + 1][hw]);
+#pragma unroll
+        for (int x = 0; x < W32; ++x) {
+          // (dim 2x of token 2j, of token 2j+1) and (dim 2x+1 of each)
+          const uint32_t lo = __builtin_amdgcn_perm(vb16[2 * j + 1][x], vb16[2 * j][x], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(vb16[2 * j + 1][x], vb16[2 * j][x], 0x07060302u);
+#pragma unroll
+          for (int hw = 0; hw < HW; ++hw) {
+            acc[hw][2 * x] = dot2_bf16(pp[hw], lo, acc[hw][2 * x]);
+            acc[hw][2 * x + 1] = dot2_bf16(pp[hw], hi, acc[hw][2 * x + 1]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float vf[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[e] = __uint_as_float(vw[i][e]);
+#pragma unroll
+        for (int hw = 0; hw < HW; ++hw)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[hw][e] = fmaf(p[i][hw], vf[e], acc[hw][e]);
+      }
     }
   }
 };
