@@ -24,6 +24,7 @@
 //      kernel would need device-scope fences that write back and invalidate the L2 on
 //      every piece: measured slower than this second launch.)
 #include "decode_common.h"
+#include "decode_mfma.h"
 
 namespace gqa {
 
@@ -73,12 +74,12 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ context_
     const unsigned long long hit = __ballot(base + (long)Hkv * incl > x);
     if (hit) {
       const int L = __ffsll((long long)hit) - 1;
-      b = c + L;
-      np = __shfl(n, L);
-      seq_base = base + (long)Hkv * (__shfl(incl, L) - np);
+      b = uniform(c + L);
+      np = uniform(__shfl(n, L));
+      seq_base = base + (long)Hkv * (uniform(__shfl(incl, L)) - np);
       return;
     }
-    base += (long)Hkv * __shfl(incl, kWave - 1);
+    base += (long)Hkv * uniform(__shfl(incl, kWave - 1));
   }
 }
 
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   // ---- total item count N = Hkv * sum_b ceil(T_b / P) ----
   long part = 0;
   for (int bb = lane; bb < B; bb += kWave) part += pages_of(context_lens, bb, max_pages, append);
-  const long N = (long)Hkv * wave_sum(part);
+  const long N = uniform((long)Hkv * wave_sum(part));
 
   if (N == 0) return;
   const long lo = share_lo(N, gw, nw);
@@ -147,31 +148,47 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     }
   };
 
-  uint32_t kb[3][4][W32], vb[3][4][W32];
+  // bf16 queries: scores on the matrix core (WaveStateMq, K in its operand layout);
+  // fp32: the vector path
+  constexpr bool kMq = sizeof(T) == 2;
+  using WS = std::conditional_t<kMq, WaveStateMq<T, D, G, TKV>, WaveState<T, D, G, TKV>>;
+  const int qsel = kMq ? lane : qd;  // what init() takes
+  // page buffers in VGPRs: NB - 1 pages in flight while one is computed (16-bit caches:
+  // 4, which leaves one wave per SIMD with D = 128 and measured faster than two waves with
+  // 3; 8-bit caches: 3; fp32 with D = 128 and 8 heads: 2, which fits 512 VGPRs)
+  constexpr int NB = sizeof(TKV) == 2 ? 4 : (sizeof(TKV) == 4 && D * G >= 1024 ? 2 : 3);
+  uint32_t kb[NB][WS::KROWS][WS::KWORDS], vb[NB][4][W32];
   // append: the row of the step's own token (slot (L - 1) % P of the sequence's last page)
   // is read from k_new / v_new instead of the pool (the pool gets it in consume()).
   auto load_page = [&](int buf, int cb, int ckv, int cpg) {
-    const size_t off = (size_t)page_table[(size_t)cb * max_pages + cpg] * page_stride +
-                       (size_t)ckv * S::PAGE + r * S::ROW;
-    const char* kp = (const char*)k_cache + off;
-    const char* vp = (const char*)v_cache + off;
+    const size_t page_off = (size_t)page_table[(size_t)cb * max_pages + cpg] * page_stride +
+                            (size_t)ckv * S::PAGE;
+    const char* kpage = (const char*)k_cache + page_off;
+    const char* kp = kpage + r * S::ROW;
+    const char* vp = (const char*)v_cache + page_off + r * S::ROW;
     int new_row = -1;
     if constexpr (APPEND) {
       const int L = seq_len(context_lens, cb, max_pages, 1);
       if (cpg == (L - 1) / kPage) new_row = (L - 1) % kPage;
     }
     const size_t new_off = ((size_t)cb * Hkv + ckv) * S::ROW;
+    if constexpr (kMq) {
+      const int kr = WS::k_row(lane);
+      WS::load_k(kr == new_row ? (const char*)k_new + new_off : kpage + kr * S::ROW, lane,
+                 kb[buf]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool nr = 4 * i + r == new_row;
-      load_row<TKV, D>(nr ? (const char*)k_new + new_off : kp + i * 4 * S::ROW, qd, kb[buf][i]);
+      if constexpr (!kMq)
+        load_row<TKV, D>(nr ? (const char*)k_new + new_off : kp + i * 4 * S::ROW, qd, kb[buf][i]);
       load_row<TKV, D>(nr ? (const char*)v_new + new_off : vp + i * 4 * S::ROW, qd, vb[buf][i]);
     }
   };
 
-  WaveState<T, D, G, TKV> st;
+  WS st;
   long seg_start = lo;  // first item of the current segment
-  st.init(q + ((size_t)b * Hq + kvh * G) * D, qd, scale_log2 < 0.f);
+  st.init(q + ((size_t)b * Hq + kvh * G) * D, qsel, scale_log2 < 0.f);
   int T_b = seq_len(context_lens, b, max_pages, append);
 
   auto store_row = [&](T* dst, int hw, float inv) {
@@ -220,10 +237,13 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
       const int slot = (T_b - 1) % kPage;
       const size_t off = (size_t)page_table[(size_t)b * max_pages + pg] * page_stride +
                          (size_t)kvh * S::PAGE + (size_t)slot * S::ROW;
+      if constexpr (kMq) {
+        if (WS::k_row(lane) == slot) WS::store_k((char*)k_store + off, lane, kb[buf]);
+      }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         if (4 * ii + r == slot) {
-          store_kv_row<TKV, D>((char*)k_store + off, qd, kb[buf][ii]);
+          if constexpr (!kMq) store_kv_row<TKV, D>((char*)k_store + off, qd, kb[buf][ii]);
           store_kv_row<TKV, D>((char*)v_store + off, qd, vb[buf][ii]);
         }
       }
@@ -238,38 +258,37 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     advance(b, kvh, pg, np);
     if (unit_end && i + 1 < hi) {
       seg_start = i + 1;
-      st.init(q + ((size_t)b * Hq + kvh * G) * D, qd, scale_log2 < 0.f);
+      st.init(q + ((size_t)b * Hq + kvh * G) * D, qsel, scale_log2 < 0.f);
       T_b = seq_len(context_lens, b, max_pages, append);
     }
   };
 
-  // The load cursor runs two items ahead of the compute cursor (three page buffers). The
+  // The load cursor runs NB - 1 items ahead of the compute cursor (NB page buffers). The
   // prefetch is issued on every step (past the share's end it re-reads the current page,
   // an L2 hit) so that the loads in flight are the same on every path and the wait before
-  // each page is exactly "all but the two newest pages".
+  // each page is exactly "all but the NB - 2 newest pages".
   int lb = b, lkv = kvh, lpg = pg, lnp = np;
   load_page(0, lb, lkv, lpg);
-  if (lo + 1 < hi) advance(lb, lkv, lpg, lnp);
-  load_page(1, lb, lkv, lpg);
-  for (long i = lo; i < hi; i += 3) {
-    if (i + 2 < hi) advance(lb, lkv, lpg, lnp);
-    load_page(2, lb, lkv, lpg);
-    consume(0, i);
-    if (i + 1 >= hi) break;
-    if (i + 3 < hi) advance(lb, lkv, lpg, lnp);
-    load_page(0, lb, lkv, lpg);
-    consume(1, i + 1);
-    if (i + 2 >= hi) break;
-    if (i + 4 < hi) advance(lb, lkv, lpg, lnp);
-    load_page(1, lb, lkv, lpg);
-    consume(2, i + 2);
+#pragma unroll
+  for (int k = 1; k < NB - 1; ++k) {
+    if (lo + k < hi) advance(lb, lkv, lpg, lnp);
+    load_page(k, lb, lkv, lpg);
+  }
+  for (long i = lo; i < hi; i += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (i + k + NB - 1 < hi) advance(lb, lkv, lpg, lnp);
+      load_page((k + NB - 1) % NB, lb, lkv, lpg);
+      consume(k, i + k);
+      if (i + k + 1 >= hi) break;
+    }
   }
 }
 
 // ---- fix-up: merge the pieces of cut units; zero rows of empty sequences ----------------
 // One wave per (sequence, KV head) unit. Lane p holds piece p's LSEs (all heads); the
-// weights come from wave reductions; each lane then sums its D / 64 dims over the pieces
-// with the loads of four pieces in flight at a time. Pieces are taken 64 at a time.
+// weights come from wave reductions; each lane then sums its D / 64 dims over the pieces.
+// Pieces are taken 64 at a time.
 constexpr int kFixupWaves = 4;
 
 template <typename T, int D, int G>
@@ -313,20 +332,42 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
 #pragma unroll
     for (int j = 0; j < DL; ++j) num[hl][j] = 0.f;
   }
+  // Pieces are read KB at a time; the first batch is issued together with the LSE loads
+  // (it does not depend on them), so a unit of up to KB pieces costs one memory round trip
+  // after the scan. Loads of dead pieces (empty shares, past the last piece) read a valid
+  // slot and are replaced by zero.
+  constexpr int KB = G * DL <= 8 ? 8 : 4;
+  float v[KB][G][DL];
   for (int c0 = w0; c0 <= w1; c0 += kWave) {
     const int np_c = min(kWave, w1 - c0 + 1);
-    // lane p: piece c0 + p (empty shares wrote nothing: weight 0, slot never read)
+    // lane p: piece c0 + p (empty shares wrote nothing: weight 0, slot never used)
     const int w = c0 + lane;
     const bool live = lane < np_c && share_lo(N, w, nw) != share_lo(N, w + 1, nw);
     const int slot = (w == w0 && !head_is_first) ? 1 : 0;
     const int off = live ? (int)(((size_t)w * 2 + slot) * SLOT) : 0;
     float lse[G];
 #pragma unroll
-    for (int hl = 0; hl < G; ++hl) lse[hl] = live ? slots[off + hl * (D + 1) + D] : -INFINITY;
+    for (int hl = 0; hl < G; ++hl) lse[hl] = slots[off + hl * (D + 1) + D];
+    auto load_batch = [&](int p0) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int p = p0 + k;  // wave-uniform
+        const int po = __shfl(off, p & (kWave - 1));
+        const bool pl = p < np_c && __shfl((int)live, p & (kWave - 1)) != 0;
+#pragma unroll
+        for (int hl = 0; hl < G; ++hl)
+#pragma unroll
+          for (int j = 0; j < DL; ++j) {
+            const float x = slots[po + hl * (D + 1) + lane + kWave * j];
+            v[k][hl][j] = pl ? x : 0.f;
+          }
+      }
+    };
+    load_batch(0);
     float wgt[G];
 #pragma unroll
     for (int hl = 0; hl < G; ++hl) {
-      float M = lse[hl];
+      float M = live ? lse[hl] : -INFINITY;
       for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
       M = fmaxf(M, m_run[hl]);
       const float rescale = m_run[hl] == -INFINITY ? 0.f
@@ -340,21 +381,19 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
       for (int j = 0; j < DL; ++j) num[hl][j] *= rescale;
       m_run[hl] = M;
     }
-    for (int p0 = 0; p0 < np_c; p0 += 4) {
+    for (int p0 = 0;;) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int p = p0 + k;  // wave-uniform
-        const int po = __shfl(off, p);
-        const bool pl = p < np_c && __shfl((int)live, p) != 0;
-        if (!pl) continue;
+      for (int k = 0; k < KB; ++k) {
 #pragma unroll
         for (int hl = 0; hl < G; ++hl) {
-          const float wv = __shfl(wgt[hl], p);
+          const float wv = __shfl(wgt[hl], (p0 + k) & (kWave - 1));
 #pragma unroll
-          for (int j = 0; j < DL; ++j)
-            num[hl][j] = fmaf(wv, slots[po + hl * (D + 1) + lane + kWave * j], num[hl][j]);
+          for (int j = 0; j < DL; ++j) num[hl][j] = fmaf(wv, v[k][hl][j], num[hl][j]);
         }
       }
+      p0 += KB;
+      if (p0 >= np_c) break;
+      load_batch(p0);
     }
   }
 #pragma unroll

@@ -110,6 +110,7 @@ struct WaveState {
   static constexpr int E = D / 16;
   static constexpr int W32 = E * (int)sizeof(T) / 4;
   static constexpr int WKV = E * (int)sizeof(TKV) / 4;  // cache words per lane per row
+  static constexpr int KROWS = 4, KWORDS = WKV;          // K words per lane per page
   uint32_t qw[HW][W32];
   float m[HW], l[HW], acc[HW][E];
 

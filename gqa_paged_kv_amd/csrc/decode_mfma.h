@@ -1,0 +1,266 @@
+// Decode wave state with the scores on the matrix core (bf16 queries; bf16 or 8-bit cache).
+//
+// The G query heads that share a KV head are the columns of one small product, the packing
+// of grouped heads into a matrix dimension that page "解锁GQA性能潜力：从批量大小敏感性到高效
+// 优化实践" (section "核心参数调优：PackGQA与NumSplits的协同舞蹈") describes: per page,
+// S^T = K_page Q^T is one chain of v_mfma_f32_16x16x32_bf16 (16 tokens x 16 columns,
+// 32 dims per step), the columns holding the group's heads repeated 16 / min(G, 4) times
+// (G = 8 takes two chains). That replaces the per-lane dot products and 16-lane DPP
+// reductions of the vector path; what the wave still does on the VALU is the softmax of
+// its own 4 scores per head and the PV products.
+//
+// Lane l (n = l % 16, g = l / 16):
+//   * K operand: token row k_row(l) = (n / 4) + 4 (n % 4) of the page, dims c*32 + g*8 .. +8
+//     of chunk c (the row permutation makes output row 4g + j the token g + 4j);
+//   * Q operand: head p*GQ + n % GQ of pass p, the same dims;
+//   * scores: tokens g + 4j (j < 4) of head p*GQ + n % GQ;
+//   * PV: V rows g + 4i (i < 4), dims of lane_dim(n, e), all G heads: the weights of the
+//     other heads come from the lanes of the same quad (DPP quad broadcast).
+// The running max is one value per head for the whole wave (raised lazily, as in the
+// vector path, by a wave-wide reduction only when some score exceeds it by 2^8), so the
+// rows of the wave need no rescaling when they are merged.
+#pragma once
+
+#include "decode_common.h"
+
+namespace gqa {
+
+template <int H>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, H * 0x55, 0xF, 0xF, false);
+}
+// lane h of each quad to the whole quad (h must fold to a constant)
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x, int h) {
+  switch (h) {
+    case 0: return quad_bcast<0>(x);
+    case 1: return quad_bcast<1>(x);
+    case 2: return quad_bcast<2>(x);
+    default: return quad_bcast<3>(x);
+  }
+}
+__device__ __forceinline__ float quad_bcast(float x, int h) {
+  return __uint_as_float(quad_bcast(__float_as_uint(x), h));
+}
+
+template <typename T, int D, int G, typename TKV = T>
+struct WaveStateMq {
+  static_assert(sizeof(T) == 2, "bf16 queries");
+  static constexpr bool kFp8 = is_fp8<TKV>();
+  static constexpr int GQ = G < 4 ? G : 4;  // heads per score chain (one per quad lane)
+  static constexpr int NPASS = G / GQ;
+  static constexpr int NC = D / 32;         // 32-dim steps of the score chain
+  static constexpr int KROWS = NC;          // K words per lane per page: KROWS x KWORDS
+  static constexpr int KWORDS = kFp8 ? 2 : 4;
+  static constexpr int E = D / 16;          // PV dims per lane
+  static constexpr int W32 = E / 2;         // bf16 words of a V row per lane
+  static constexpr int WKV = kFp8 ? W32 / 2 : W32;
+  static_assert(D % 32 == 0 && G % GQ == 0 && NPASS <= 2, "shape");
+
+  u32x4_t qb[NPASS][NC];
+  float mrun[NPASS], lrun[NPASS];  // this lane's head: reference max, this row's sum
+  float acc[G][E];
+  float m[G], l[G];                // per head, valid after merge_rows()
+
+  static __device__ __forceinline__ int k_row(int lane) {
+    const int n = lane & 15;
+    return (n >> 2) + 4 * (n & 3);
+  }
+  static __device__ __forceinline__ int k_off(int lane, int c) {
+    return kFp8 ? c * 32 + (lane >> 4) * 8 : c * 64 + (lane >> 4) * 16;
+  }
+  // this lane's words of K row `row` (the row k_row(lane) of a page)
+  static __device__ __forceinline__ void load_k(const char* row, int lane,
+                                                uint32_t (&kw)[KROWS][KWORDS]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (kFp8) {
+        const u32x2_t v = *(const u32x2_t*)(row + k_off(lane, c));
+        kw[c][0] = v[0]; kw[c][1] = v[1];
+      } else {
+        const u32x4_t v = *(const u32x4_t*)(row + k_off(lane, c));
+        kw[c][0] = v[0]; kw[c][1] = v[1]; kw[c][2] = v[2]; kw[c][3] = v[3];
+      }
+    }
+  }
+  static __device__ __forceinline__ void store_k(char* row, int lane,
+                                                 const uint32_t (&kw)[KROWS][KWORDS]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (kFp8) {
+        *(u32x2_t*)(row + k_off(lane, c)) = u32x2_t{kw[c][0], kw[c][1]};
+      } else {
+        *(u32x4_t*)(row + k_off(lane, c)) = u32x4_t{kw[c][0], kw[c][1], kw[c][2], kw[c][3]};
+      }
+    }
+  }
+
+  // q_head0: the group's first query head. neg: the caller's scale is negative; q is
+  // negated here (exact) and the kernel runs with |scale|.
+  __device__ __forceinline__ void init(const T* q_head0, int lane, bool neg) {
+    const uint32_t flip = neg ? 0x80008000u : 0u;
+    const int n = lane & 15;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const char* src = (const char*)(q_head0 + (size_t)(p * GQ + n % GQ) * D);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4_t v = *(const u32x4_t*)(src + c * 64 + (lane >> 4) * 16);
+        qb[p][c] = v ^ flip;
+      }
+    }
+    reset();
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      mrun[p] = -INFINITY;
+      lrun[p] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  }
+
+  // Merge the 4 rows (token groups) of the wave: every lane gets, for all G heads, the
+  // group's m, l and the summed acc of its dims. The whole wave must be active.
+  __device__ __forceinline__ void merge_rows() {
+    float lt[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      float x = lrun[p];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      lt[p] = x;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = quad_bcast(mrun[h / GQ], h % GQ);
+      l[h] = quad_bcast(lt[h / GQ], h % GQ);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float a = acc[h][e];
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        acc[h][e] = a;
+      }
+    }
+  }
+
+  // Consume one page. kw: this lane's K words (row k_row(lane)); vw[i]: V row g + 4i.
+  // tok0 = page start + g. MASKED: tokens >= t_end are dead (their slots may hold anything).
+  template <bool MASKED>
+  __device__ __forceinline__ void page(const uint32_t (&kw)[KROWS][KWORDS],
+                                       uint32_t (&vw)[4][WKV], int tok0, int t_end,
+                                       float scale_log2) {
+    f32x4_t s[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) s[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4_t a;
+      if constexpr (kFp8) {
+        a = u32x4_t{fp8x2_to_bf16x2<TKV>(kw[c][0], false), fp8x2_to_bf16x2<TKV>(kw[c][0], true),
+                    fp8x2_to_bf16x2<TKV>(kw[c][1], false), fp8x2_to_bf16x2<TKV>(kw[c][1], true)};
+      } else {
+        a = u32x4_t{kw[c][0], kw[c][1], kw[c][2], kw[c][3]};
+      }
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p)
+        s[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, qb[p][c]),
+                                                       s[p], 0, 0, 0);
+    }
+
+    float x[NPASS][4], mx[NPASS];
+    bool trig = false;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[p][j] = s[p][j] * scale_log2;  // raw q.k times |scale| log2 e
+        if (MASKED && tok0 + 4 * j >= t_end) x[p][j] = -INFINITY;
+      }
+      mx[p] = fmaxf(fmaxf(x[p][0], x[p][1]), fmaxf(x[p][2], x[p][3]));
+      trig |= mx[p] > mrun[p] + kLazyLog2;
+    }
+    // The reference max of a head is raised (wave-wide) only when a score exceeds it by
+    // more than 2^kLazyLog2; acc and l are rescaled then, and acc / l is unchanged.
+    if (__any(trig)) {
+      float alpha[NPASS];
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        float M = mx[p];
+#pragma unroll
+        for (int o = GQ; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+        M = fmaxf(M, __shfl_xor(M, 16));
+        M = fmaxf(M, __shfl_xor(M, 32));
+        const float m_new = fmaxf(mrun[p], M);
+        const float m_ref = (m_new > mrun[p] + kLazyLog2) ? m_new : mrun[p];
+        alpha[p] = (m_ref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun[p] - m_ref);
+        lrun[p] *= alpha[p];
+        mrun[p] = m_ref;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float a = quad_bcast(alpha[h / GQ], h % GQ);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= a;
+      }
+    }
+    // weights of this lane's head, packed as bf16 pairs of tokens (g, g+4), (g+8, g+12)
+    uint32_t pk[NPASS][2];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const float msub = mrun[p] == -INFINITY ? 0.f : mrun[p];
+      float w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_exp2f(x[p][j] - msub);
+      lrun[p] += (w[0] + w[1]) + (w[2] + w[3]);
+      pk[p][0] = pack_bf16x2(w[0], w[1]);
+      pk[p][1] = pack_bf16x2(w[2], w[3]);
+    }
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tok0 + 4 * i >= t_end) {
+#pragma unroll
+          for (int y = 0; y < WKV; ++y) vw[i][y] = 0u;  // never multiply a dead slot
+        }
+    }
+    uint32_t vb16[4][W32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int y = 0; y < WKV; ++y) {
+          vb16[i][2 * y] = fp8x2_to_bf16x2<TKV>(vw[i][y], false);
+          vb16[i][2 * y + 1] = fp8x2_to_bf16x2<TKV>(vw[i][y], true);
+        }
+      } else {
+#pragma unroll
+        for (int y = 0; y < W32; ++y) vb16[i][y] = vw[i][y];
+      }
+    }
+    // PV on bf16 pairs (tokens 2j', 2j'+1 of this lane's rows), fp32 accumulation
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      uint32_t pp[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pp[h] = quad_bcast(pk[h / GQ][jp], h % GQ);
+#pragma unroll
+      for (int y = 0; y < W32; ++y) {
+        const uint32_t lo = __builtin_amdgcn_perm(vb16[2 * jp + 1][y], vb16[2 * jp][y], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(vb16[2 * jp + 1][y], vb16[2 * jp][y], 0x07060302u);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][2 * y] = dot2_bf16(pp[h], lo, acc[h][2 * y]);
+          acc[h][2 * y + 1] = dot2_bf16(pp[h], hi, acc[h][2 * y + 1]);
+        }
+      }
+    }
+  }
+};
+
+}  // namespace gqa

@@ -128,4 +128,14 @@ __device__ __forceinline__ int wave_id() {
 }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// A value every lane of the wave holds, moved to a scalar register: the compiler then
+// treats what derives from it as wave-uniform (scalar loads and branches).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ long uniform(long x) {
+  const unsigned long long u = (unsigned long long)x;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(u & 0xffffffffu));
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(u >> 32));
+  return (long)(((unsigned long long)hi << 32) | lo);
+}
+
 }  // namespace gqa

@@ -310,6 +310,35 @@ def test_balanced_config5(gpu_lib, B, Hkv):
     assert_close(got, want, "bf16", f"balanced config5 B={B} Hkv={Hkv}")
 
 
+def test_balanced_workspace_reused_across_shapes(gpu_lib):
+    """One workspace serves a run of calls with different head shapes and length mixes (units
+    cut into 2 pieces, into hundreds of pieces, empty sequences, the G >= 16 split path in
+    between): every result matches the oracle and rows of empty sequences are written as
+    zeros over a NaN-filled output."""
+    import gqa_paged_kv_amd as gk
+    ws = gk.balanced_workspace(64, 32, 1, 128, DEV)  # the largest shape below (G = 32)
+    cases = [
+        ("bf16", 32, 8, [37, 300, 16, 0, 1000, 5, 0, 64]),
+        ("bf16", 32, 8, [4096]),          # one sequence: each unit cut into many pieces
+        ("bf16", 32, 2, [33] * 40),       # G = 16: split path
+        ("f32", 8, 2, [0, 257, 1, 3000, 0, 17]),
+        ("bf16", 8, 8, [2000, 0, 999]),   # G = 1
+        ("bf16", 32, 8, [37, 300, 16, 0, 1000, 5, 0, 64]),
+    ]
+    for i, (dtype, hq, hkv, lens) in enumerate(cases):
+        print(f"[balanced] workspace reuse {i} {dtype} {hq}x{hkv} B={len(lens)}", flush=True)
+        x = synth.decode_inputs(len(lens), hq, hkv, 128, 16, lens, dtype, seed=500 + i,
+                                device=DEV)
+        out = torch.full_like(x.q, float("nan"))
+        gpu_lib.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
+                                      scale=x.scale, out=out, workspace=ws)
+        _sync()
+        assert_close(out, _ref(x), dtype, f"workspace reuse case {i}")
+        for b, t in enumerate(lens):
+            if t == 0:
+                assert torch.all(out[b] == 0), f"case {i}: empty sequence {b} not zeroed"
+
+
 # ---------------------------------------------------------------- scale sign and magnitude
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.7])
