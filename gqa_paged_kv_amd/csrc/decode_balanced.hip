@@ -52,6 +52,15 @@ __device__ __forceinline__ long wave_sum(long x) {
   return x;
 }
 
+// Waves that take a share: all resident waves, or fewer when the batch is small, so that
+// a share holds at least kMinShare items (tiny shares cost more in start-up and in pieces
+// to merge than they save in parallelism).
+constexpr long kMinShare = 4;
+__device__ __forceinline__ int active_waves(long N, int resident) {
+  const long w = N / kMinShare;
+  return w < 1 ? 1 : (w < resident ? (int)w : resident);
+}
+
 // share bounds and owner of an item (integer arithmetic shared by writers and mergers)
 __device__ __forceinline__ long share_lo(long N, int w, int nw) { return N * w / nw; }
 __device__ __forceinline__ int share_owner(long N, long x, int nw) {
@@ -110,7 +119,6 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   const int lane = lane_id();
   const int r = lane >> 4;
   const int qd = lane & 15;
-  const int nw = gridDim.x * kDecodeWaves;
   const int gw = blockIdx.x * kDecodeWaves + wave_id();
 
   // ---- total item count N = Hkv * sum_b ceil(T_b / P) ----
@@ -119,6 +127,8 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   const long N = uniform((long)Hkv * wave_sum(part));
 
   if (N == 0) return;
+  const int nw = active_waves(N, gridDim.x * kDecodeWaves);
+  if (gw >= nw) return;  // no share: items [N gw / nw, ...) would lie past the last item
   const long lo = share_lo(N, gw, nw);
   const long hi = share_lo(N, gw + 1, nw);
   if (lo >= hi) return;
@@ -286,9 +296,11 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
 }
 
 // ---- fix-up: merge the pieces of cut units; zero rows of empty sequences ----------------
-// One wave per (sequence, KV head) unit. Lane p holds piece p's LSEs (all heads); the
-// weights come from wave reductions; each lane then sums its D / 64 dims over the pieces.
-// Pieces are taken 64 at a time.
+// One wave per (sequence, KV head, query head of the group). Lane p holds piece p's LSE;
+// the weights come from wave reductions; each lane then sums its D / 64 dims over the
+// pieces, KB pieces per batch, the first batch's loads issued together with the LSE loads
+// (they do not depend on them), so a unit cut into up to KB pieces costs one memory round
+// trip after the page-count scan. Pieces are taken 64 at a time.
 constexpr int kFixupWaves = 4;
 
 template <typename T, int D, int G>
@@ -297,9 +309,12 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
     T* __restrict__ out, int B, int Hq, int Hkv, int max_pages, int nw, int append) {
   constexpr int SLOT = G * (D + 1);
   constexpr int DL = D / kWave;  // dims per lane
+  constexpr int KB = 32;         // pieces per batch
   const int lane = lane_id();
-  const long u = (long)blockIdx.x * kFixupWaves + wave_id();
-  if (u >= (long)B * Hkv) return;
+  const long t = (long)blockIdx.x * kFixupWaves + wave_id();
+  if (t >= (long)B * Hkv * G) return;
+  const long u = t / G;  // (sequence, KV head) unit
+  const int hl = (int)(t % G);
   const int b = (int)(u / Hkv);
   const int kvh = (int)(u % Hkv);
   // N and the first item of sequence b in one pass over the page counts
@@ -310,11 +325,14 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
     part_before += bb < b ? n : 0;
   }
   const long N = (long)Hkv * wave_sum(part_all);
+  nw = active_waves(N, nw);
   const int np = pages_of(context_lens, b, max_pages, append);
-  T* dst = out + ((size_t)b * Hq + kvh * G) * D;
+  T* dst = out + ((size_t)b * Hq + kvh * G + hl) * D;
   if (np == 0) {  // T_b == 0: the output is zero
-    for (int i = lane; i < G * D; i += kWave) {
-      if constexpr (sizeof(T) == 2) ((uint16_t*)dst)[i] = 0; else dst[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DL; ++j) {
+      if constexpr (sizeof(T) == 2) ((uint16_t*)dst)[lane + kWave * j] = 0;
+      else dst[lane + kWave * j] = 0.f;
     }
     return;
   }
@@ -324,88 +342,63 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
   if (w0 == w1) return;  // finished and written by its wave
   const bool head_is_first = share_lo(N, w0, nw) == first;
 
-  float m_run[G], den[G], num[G][DL];
+  float m_run = -INFINITY, den = 0.f, num[DL];
 #pragma unroll
-  for (int hl = 0; hl < G; ++hl) {
-    m_run[hl] = -INFINITY;
-    den[hl] = 0.f;
-#pragma unroll
-    for (int j = 0; j < DL; ++j) num[hl][j] = 0.f;
-  }
-  // Pieces are read KB at a time; the first batch is issued together with the LSE loads
-  // (it does not depend on them), so a unit of up to KB pieces costs one memory round trip
-  // after the scan. Loads of dead pieces (empty shares, past the last piece) read a valid
-  // slot and are replaced by zero.
-  constexpr int KB = G * DL <= 8 ? 8 : 4;
-  float v[KB][G][DL];
+  for (int j = 0; j < DL; ++j) num[j] = 0.f;
+  float v[KB][DL];
   for (int c0 = w0; c0 <= w1; c0 += kWave) {
     const int np_c = min(kWave, w1 - c0 + 1);
     // lane p: piece c0 + p (empty shares wrote nothing: weight 0, slot never used)
     const int w = c0 + lane;
     const bool live = lane < np_c && share_lo(N, w, nw) != share_lo(N, w + 1, nw);
     const int slot = (w == w0 && !head_is_first) ? 1 : 0;
-    const int off = live ? (int)(((size_t)w * 2 + slot) * SLOT) : 0;
-    float lse[G];
-#pragma unroll
-    for (int hl = 0; hl < G; ++hl) lse[hl] = slots[off + hl * (D + 1) + D];
+    const int off = live ? (int)(((size_t)w * 2 + slot) * SLOT) + hl * (D + 1) : 0;
+    const float lse = slots[off + D];
+    // data of KB pieces; dead pieces read a valid slot and are replaced by zero
     auto load_batch = [&](int p0) {
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
-        const int p = p0 + k;  // wave-uniform
-        const int po = __shfl(off, p & (kWave - 1));
-        const bool pl = p < np_c && __shfl((int)live, p & (kWave - 1)) != 0;
+        const int p = (p0 + k) & (kWave - 1);
+        const int po = __builtin_amdgcn_readlane(off, p);
+        const bool pl = p0 + k < np_c && __builtin_amdgcn_readlane((int)live, p) != 0;
 #pragma unroll
-        for (int hl = 0; hl < G; ++hl)
-#pragma unroll
-          for (int j = 0; j < DL; ++j) {
-            const float x = slots[po + hl * (D + 1) + lane + kWave * j];
-            v[k][hl][j] = pl ? x : 0.f;
-          }
+        for (int j = 0; j < DL; ++j) {
+          const float x = slots[po + lane + kWave * j];
+          v[k][j] = pl ? x : 0.f;
+        }
       }
     };
     load_batch(0);
-    float wgt[G];
+    float M = live ? lse : -INFINITY;
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    M = fmaxf(M, m_run);
+    const float rescale = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * kLog2e);
+    const float wgt = live ? __builtin_amdgcn_exp2f((lse - M) * kLog2e) : 0.f;
+    float ws = wgt;
+    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+    den = den * rescale + ws;
 #pragma unroll
-    for (int hl = 0; hl < G; ++hl) {
-      float M = live ? lse[hl] : -INFINITY;
-      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-      M = fmaxf(M, m_run[hl]);
-      const float rescale = m_run[hl] == -INFINITY ? 0.f
-                            : __builtin_amdgcn_exp2f((m_run[hl] - M) * kLog2e);
-      wgt[hl] = live ? __builtin_amdgcn_exp2f((lse[hl] - M) * kLog2e) : 0.f;
-      den[hl] *= rescale;
-      float ws = wgt[hl];
-      for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
-      den[hl] += ws;
-#pragma unroll
-      for (int j = 0; j < DL; ++j) num[hl][j] *= rescale;
-      m_run[hl] = M;
-    }
+    for (int j = 0; j < DL; ++j) num[j] *= rescale;
+    m_run = M;
     for (int p0 = 0;;) {
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
+        const float wv = __builtin_amdgcn_readlane(__float_as_int(wgt), (p0 + k) & (kWave - 1));
 #pragma unroll
-        for (int hl = 0; hl < G; ++hl) {
-          const float wv = __shfl(wgt[hl], (p0 + k) & (kWave - 1));
-#pragma unroll
-          for (int j = 0; j < DL; ++j) num[hl][j] = fmaf(wv, v[k][hl][j], num[hl][j]);
-        }
+        for (int j = 0; j < DL; ++j) num[j] = fmaf(__int_as_float(wv), v[k][j], num[j]);
       }
       p0 += KB;
       if (p0 >= np_c) break;
       load_batch(p0);
     }
   }
+  const float inv = 1.0f / den;
 #pragma unroll
-  for (int hl = 0; hl < G; ++hl) {
-    const float inv = 1.0f / den[hl];
-#pragma unroll
-    for (int j = 0; j < DL; ++j) {
-      const float o = num[hl][j] * inv;
-      const int d = lane + kWave * j;
-      if constexpr (sizeof(T) == 2) ((uint16_t*)(dst + hl * D))[d] = f32_to_bf16(o);
-      else dst[hl * D + d] = o;
-    }
+  for (int j = 0; j < DL; ++j) {
+    const float o = num[j] * inv;
+    const int d = lane + kWave * j;
+    if constexpr (sizeof(T) == 2) ((uint16_t*)dst)[d] = f32_to_bf16(o);
+    else dst[d] = o;
   }
 }
 
@@ -440,7 +433,7 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
                      (const T*)q, (const TKV*)k, (const TKV*)v, pt, lens, (T*)out, slots, B, Hq,
                      Hkv, max_pages, scale * kLog2e, out_scale, (const TKV*)k_new,
                      (const TKV*)v_new, (TKV*)k_store, (TKV*)v_store);
-  const unsigned fix_grid = (unsigned)(((long)B * Hkv + kFixupWaves - 1) / kFixupWaves);
+  const unsigned fix_grid = (unsigned)(((long)B * Hq + kFixupWaves - 1) / kFixupWaves);
   hipLaunchKernelGGL((fixup_kernel<T, D, G>), dim3(fix_grid), dim3(kFixupWaves * kWave), 0, s,
                      slots, lens, (T*)out, B, Hq, Hkv, max_pages, grid * kDecodeWaves,
                      APPEND ? 1 : 0);

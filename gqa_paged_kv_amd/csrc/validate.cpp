@@ -77,10 +77,14 @@ int gqa_validate_decode(const void* q, const void* k_cache, const void* v_cache,
   return GQA_OK;
 }
 
-// Split count used by the balanced entry point when G >= 16 (the LDS-staged split path).
+// Split count used by the balanced entry point when G >= 16 (the LDS-staged split path,
+// one workgroup per (sequence, KV head, split)): enough splits for one workgroup per CU of
+// the 256-CU MI355X and no more. Measured with B x Hkv from 1 to 256 (Hq = 32, T = 1024):
+// fewer splits leave CUs idle, more add combine traffic and shorter per-split streams.
 int gqa_balanced_auto_splits(int B, int Hkv) {
   const long units = (long)B * Hkv;
-  long ns = (1024 + units - 1) / units;
+  if (units <= 0) return 1;
+  long ns = (256 + units - 1) / units;
   return (int)(ns < 1 ? 1 : (ns > 16 ? 16 : ns));
 }
 

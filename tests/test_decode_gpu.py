@@ -310,6 +310,16 @@ def test_balanced_config5(gpu_lib, B, Hkv):
     assert_close(got, want, "bf16", f"balanced config5 B={B} Hkv={Hkv}")
 
 
+@pytest.mark.parametrize("B,hq,hkv,T", [(1, 32, 8, 1024), (1, 32, 32, 1024), (2, 8, 2, 100),
+                                         (1, 4, 1, 16), (3, 32, 8, 40)])
+def test_balanced_small_batches_use_fewer_waves(gpu_lib, B, hq, hkv, T):
+    """Batches with fewer than a few pages per resident wave: only N / 4 waves take a share
+    (the others must return at once) and the fix-up uses the same partition."""
+    print(f"[balanced] small batch B={B} {hq}x{hkv} T={T}", flush=True)
+    x = synth.decode_inputs(B, hq, hkv, 128, 16, [T] * B, "bf16", seed=B * 31 + T, device=DEV)
+    assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"small batch B={B} T={T}")
+
+
 def test_balanced_workspace_reused_across_shapes(gpu_lib):
     """One workspace serves a run of calls with different head shapes and length mixes (units
     cut into 2 pieces, into hundreds of pieces, empty sequences, the G >= 16 split path in
