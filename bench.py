@@ -284,7 +284,8 @@ def main():
             "median_us": round(f8med * 1e3, 2),
             "gbs": round(f8gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(f8gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(f8gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(f8gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_balanced_fp8e4m3_B64_Hq32_Hkv8"),
                          "kernel": "balanced_kernel<bf16,128,4,fp8e4m3> + fixup_kernel"},
         }
         del f8, f8out, f8ws
@@ -342,7 +343,7 @@ def main():
             "tflops": round(ctf, 1),
             "roofline": {"bound": "mfma", "achieved": round(ctf, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ctf / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": measured_traffic("prefill_paged_bf16_B4_P4096_N512_Hq32_Hkv8"),
                          "kernel": "append_at_kernel + prefill_causal_kernel<4, paged> (one call)"},
             "flops_per_call": cfl,
         }
