@@ -69,12 +69,14 @@ __device__ __forceinline__ int share_owner(long N, long x, int nw) {
 
 // First sequence b whose items end past item x (so np_b > 0), with np_b and the index of
 // its first item: wave-wide inclusive scans of ceil(T_b / P), 64 sequences per step.
+// n_first: this lane's page count of the first 64 sequences (already loaded by the caller).
 __device__ __forceinline__ void locate_item(const int32_t* __restrict__ context_lens, int B,
                                             int Hkv, int max_pages, int append, long x, int lane,
-                                            int& b, int& np, long& seq_base) {
+                                            int n_first, int& b, int& np, long& seq_base) {
   long base = 0;
   for (int c = 0; c < B; c += kWave) {
-    const int n = c + lane < B ? pages_of(context_lens, c + lane, max_pages, append) : 0;
+    const int n = c == 0 ? n_first
+                         : (c + lane < B ? pages_of(context_lens, c + lane, max_pages, append) : 0);
     int incl = n;
     for (int off = 1; off < kWave; off <<= 1) {
       const int v = __shfl_up(incl, off);
@@ -90,14 +92,6 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ context_
     }
     base += (long)Hkv * uniform(__shfl(incl, kWave - 1));
   }
-}
-
-// Index of the first item of sequence b (exclusive scan up to b).
-__device__ __forceinline__ long items_before(const int32_t* __restrict__ context_lens, int b,
-                                             int Hkv, int max_pages, int append, int lane) {
-  long part = 0;
-  for (int bb = lane; bb < b; bb += kWave) part += pages_of(context_lens, bb, max_pages, append);
-  return (long)Hkv * wave_sum(part);
 }
 
 // T: q / out element type; TKV: cache element type (T, or an 8-bit float whose per-tensor
@@ -122,8 +116,10 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   const int gw = blockIdx.x * kDecodeWaves + wave_id();
 
   // ---- total item count N = Hkv * sum_b ceil(T_b / P) ----
-  long part = 0;
-  for (int bb = lane; bb < B; bb += kWave) part += pages_of(context_lens, bb, max_pages, append);
+  const int n_first = lane < B ? pages_of(context_lens, lane, max_pages, append) : 0;
+  long part = n_first;
+  for (int bb = lane + kWave; bb < B; bb += kWave)
+    part += pages_of(context_lens, bb, max_pages, append);
   const long N = uniform((long)Hkv * wave_sum(part));
 
   if (N == 0) return;
@@ -136,7 +132,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   // ---- locate the sequence holding item lo ----
   int b = 0, np = 1;
   long seq_base = 0;  // first item of sequence b
-  locate_item(context_lens, B, Hkv, max_pages, append, lo, lane, b, np, seq_base);
+  locate_item(context_lens, B, Hkv, max_pages, append, lo, lane, n_first, b, np, seq_base);
   const long rem = lo - seq_base;
   int kvh = (int)(rem / np);
   int pg = (int)(rem % np);
