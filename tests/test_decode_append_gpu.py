@@ -108,3 +108,19 @@ def test_decode_append_with_shared_prefix(gpu_lib):
     out = _step(gpu_lib, xd, kn.to(DEV), vn.to(DEV))
     assert_close(out, ref, "bf16", "append shared prefix")
     assert torch.equal(xd.k_cache.cpu().view(torch.int16), kc.view(torch.int16))
+
+
+def test_decode_append_at_capacity_and_clamped(gpu_lib):
+    """The page-table row addresses 48 tokens (3 pages): a sequence holding 47 tokens appends
+    into the very last slot; a length past the row is clamped so that the append still lands
+    in the last slot and the step attends all 48 tokens."""
+    print("[append] capacity / clamp", flush=True)
+    x, kn, vn = _inputs("bf16", 32, 8, 128, [47, 47], seed=77)
+    assert x.page_table.shape[1] == 3
+    ref, kc, vc = _reference(x, kn, vn)
+    xd = x.to(DEV)
+    xd.context_lens = torch.tensor([47, 5000], dtype=torch.int32, device=DEV)
+    out = _step(gpu_lib, xd, kn.to(DEV), vn.to(DEV))
+    assert_close(out, ref, "bf16", "append at capacity / clamped")
+    assert torch.equal(xd.k_cache.cpu().view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(xd.v_cache.cpu().view(torch.int16), vc.view(torch.int16))

@@ -320,6 +320,28 @@ def test_balanced_small_batches_use_fewer_waves(gpu_lib, B, hq, hkv, T):
     assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"small batch B={B} T={T}")
 
 
+def test_balanced_all_sequences_empty_and_clamped_lengths(gpu_lib):
+    """A batch with no cached token at all (the kernels see N = 0 items) gives zero rows over
+    a NaN-filled output; lengths past what the page-table row addresses are clamped to it."""
+    print("[balanced] all empty / clamped", flush=True)
+    for dtype, hq, hkv in (("bf16", 32, 8), ("f32", 8, 2), ("bf16", 32, 2)):
+        x = synth.decode_inputs(3, hq, hkv, 128, 16, [0, 0, 0], dtype, seed=61, device=DEV)
+        out = torch.full_like(x.q, float("nan"))
+        gpu_lib.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
+                                      scale=x.scale, out=out)
+        _sync()
+        assert torch.all(out == 0), f"all empty {dtype} {hq}x{hkv}"
+    # max_pages = 4: rows 1 and 2 hold 4 live pages (64 tokens), row 0 three (40 tokens);
+    # only rows whose table is full get a length past it
+    x = synth.decode_inputs(3, 32, 8, 128, 16, [40, 64, 64], "bf16", seed=62, device=DEV)
+    ref = _ref(x)
+    big = torch.tensor([40, 10_000, 2**30], dtype=torch.int32, device=DEV)
+    out = gpu_lib.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, big,
+                                        scale=x.scale)
+    _sync()
+    assert_close(out, ref, "bf16", "balanced clamped lengths")
+
+
 def test_balanced_workspace_reused_across_shapes(gpu_lib):
     """One workspace serves a run of calls with different head shapes and length mixes (units
     cut into 2 pieces, into hundreds of pieces, empty sequences, the G >= 16 split path in

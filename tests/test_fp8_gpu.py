@@ -63,3 +63,25 @@ def test_fp8_decode_scales_fold_exactly(gpu_lib):
     x.k_scale *= 2.0
     x.v_scale *= 0.5
     assert_close(_run(gpu_lib, x), _ref(x), "bf16", "fp8 rescaled")
+
+
+def test_fp8_decode_all_empty_and_clamped(gpu_lib):
+    """No cached token in the whole batch: zero rows over a NaN-filled output. Lengths past
+    what the page table addresses are clamped to it."""
+    print("[fp8] all empty / clamped", flush=True)
+    x = synth.fp8_decode_inputs(2, 32, 8, 128, 16, [0, 0], "e4m3", seed=63, device=DEV)
+    out = torch.full_like(x.q, float("nan"))
+    gpu_lib.decode_paged_fp8(x.q, x.k_cache, x.v_cache, x.k_scale, x.v_scale, x.page_table,
+                             x.context_lens, fmt=x.fmt, scale=x.scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    y = synth.fp8_decode_inputs(2, 32, 8, 128, 16, [30, 48], "e5m2", seed=64, device=DEV)
+    c = y.to("cpu")
+    big = torch.tensor([30, 1_000_000], dtype=torch.int32, device=DEV)  # 3 pages per row
+    got = gpu_lib.decode_paged_fp8(y.q, y.k_cache, y.v_cache, y.k_scale, y.v_scale,
+                                   y.page_table, big, fmt=y.fmt, scale=y.scale)
+    torch.cuda.synchronize()
+    want = oracle.decode_paged_fp8(c.q, c.k_cache, c.v_cache, c.k_scale, c.v_scale,
+                                   c.page_table, torch.tensor([30, 48], dtype=torch.int32),
+                                   c.scale, c.fmt)
+    assert_close(got, want, "bf16", "fp8 clamped")
