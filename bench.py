@@ -372,31 +372,38 @@ def main():
 
 
 def sweep(g, synth, dev, stream):
-    """Extra JSON lines: long-context split sweep and batch/group sweep (event medians)."""
+    """Extra JSON lines: long-context split sweep and batch/group sweep. Every call is timed
+    alone with HIP events after a 1 GiB streaming read that evicts the L2 and the Infinity
+    Cache (the long-context B=1 pool, 134 MB, would otherwise stay in the 256 MB cache);
+    median and 10th / 90th percentile of 20 calls."""
+    scratch = torch.ones(1024 * 2**20 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
+    flush = lambda: g.bench_stream_read(scratch, sink, 8, 1)
+
+    def timed(f, nb, **fields):
+        for _ in range(3):
+            f()
+        ts = sorted(event_times(f, 20, stream, flush=flush))
+        t = statistics.median(ts)
+        print(json.dumps({**fields, "us": round(t * 1e3, 2), "p10_us": round(ts[2] * 1e3, 2),
+                          "p90_us": round(ts[17] * 1e3, 2),
+                          "gbs": round(nb / (t * 1e-3) / 1e9, 1)}), flush=True)
+
     for B in synth.CONFIG4_BATCHES:
         x = synth.config4(B, device=dev)
         nb = kv_bytes(x)
         bws = g.balanced_workspace(B, 32, 8, 128, dev)
         out = torch.empty_like(x.q)
-        f = lambda: g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table,
-                                            x.context_lens, scale=x.scale, out=out, workspace=bws)
-        for _ in range(3):
-            f()
-        t = statistics.median(event_times(f, 20, stream))
-        print(json.dumps({"sweep": "long-context", "B": B, "T": 32768, "partition": "balanced",
-                          "us": round(t * 1e3, 2), "gbs": round(nb / (t * 1e-3) / 1e9, 1)}),
-              flush=True)
+        timed(lambda: g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table,
+                                              x.context_lens, scale=x.scale, out=out,
+                                              workspace=bws),
+              nb, sweep="long-context", B=B, T=32768, partition="balanced")
         for ns in synth.CONFIG4_SPLITS:
             ws = g.alloc_workspace(B, 32, 128, ns, dev) if ns > 1 else None
-            out = torch.empty_like(x.q)
-            f = lambda: g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
-                                       num_splits=ns, scale=x.scale, out=out, workspace=ws)
-            for _ in range(3):
-                f()
-            t = statistics.median(event_times(f, 20, stream))
-            print(json.dumps({"sweep": "long-context", "B": B, "T": 32768, "num_splits": ns,
-                              "us": round(t * 1e3, 2), "gbs": round(nb / (t * 1e-3) / 1e9, 1)}),
-                  flush=True)
+            timed(lambda: g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table,
+                                         x.context_lens, num_splits=ns, scale=x.scale, out=out,
+                                         workspace=ws),
+                  nb, sweep="long-context", B=B, T=32768, num_splits=ns)
         del x
     for hkv in synth.CONFIG5_KV_HEADS:
         for B in synth.CONFIG5_BATCHES:
@@ -404,29 +411,18 @@ def sweep(g, synth, dev, stream):
             nb = kv_bytes(x)
             bws = g.balanced_workspace(B, 32, hkv, 128, dev)
             out = torch.empty_like(x.q)
-            f = lambda: g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table,
-                                                x.context_lens, scale=x.scale, out=out,
-                                                workspace=bws)
-            for _ in range(3):
-                f()
-            t = statistics.median(event_times(f, 20, stream))
-            print(json.dumps({"sweep": "batch-group", "B": B, "Hkv": hkv, "T": 1024,
-                              "partition": "balanced", "us": round(t * 1e3, 2),
-                              "gbs": round(nb / (t * 1e-3) / 1e9, 1)}), flush=True)
+            timed(lambda: g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table,
+                                                  x.context_lens, scale=x.scale, out=out,
+                                                  workspace=bws),
+                  nb, sweep="batch-group", B=B, Hkv=hkv, T=1024, partition="balanced")
             for ns in (1, 2, 4, 8):
                 ws = g.alloc_workspace(B, 32, 128, ns, dev) if ns > 1 else None
-                out = torch.empty_like(x.q)
-                f = lambda: g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table,
-                                           x.context_lens, num_splits=ns, scale=x.scale, out=out,
-                                           workspace=ws)
-                for _ in range(3):
-                    f()
-                t = statistics.median(event_times(f, 20, stream))
-                gbs = nb / (t * 1e-3) / 1e9
-                print(json.dumps({"sweep": "batch-group", "B": B, "Hkv": hkv, "T": 1024,
-                                  "num_splits": ns, "us": round(t * 1e3, 2), "gbs": round(gbs, 1)}),
-                      flush=True)
+                timed(lambda: g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table,
+                                             x.context_lens, num_splits=ns, scale=x.scale,
+                                             out=out, workspace=ws),
+                      nb, sweep="batch-group", B=B, Hkv=hkv, T=1024, num_splits=ns)
             del x
+    del scratch, sink
 
 
 if __name__ == "__main__":
