@@ -88,6 +88,23 @@ def test_config3_prefill_sampled_heads_and_append(gpu_lib, cfg3):
     assert_close(got, want, "bf16", "config3 sampled heads")
 
 
+def test_prefill_long_sequence_sampled_heads(gpu_lib):
+    """S = 8192 (4x the benchmark length: 128 key tiles for the last q-tile, the running max
+    raised many times): two sampled heads against the oracle, and the append of all 8192
+    positions."""
+    print("[prefill] S=8192", flush=True)
+    x = synth.prefill_inputs(1, 8192, 8, 2, 128, 16, seed=8192, device=DEV)
+    kb, vb = x.k_cache.cpu(), x.v_cache.cpu()
+    out = _run(gpu_lib, x)
+    _check_append(x, kb, vb)
+    c = x.to("cpu")
+    rows = [(0, 1), (0, 6)]
+    ref = oracle.prefill_causal_rows(c.q, c.k, c.v, c.scale, rows)
+    got = np.stack([to_f64(out[b, :, h]) for (b, h) in rows])
+    want = np.stack([ref[r] for r in rows])
+    assert_close(got, want, "bf16", "prefill S=8192 sampled heads")
+
+
 def test_config3_deterministic(gpu_lib, cfg3):
     print("[prefill] config3 determinism", flush=True)
     x, _, _ = cfg3
