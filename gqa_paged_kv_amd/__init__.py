@@ -152,10 +152,16 @@ def decode_paged(q, k_cache, v_cache, page_table, context_lens, num_splits: int 
     return out
 
 
+# Leading bytes of a balanced-decode workspace that hold counters (zero between calls).
+BALANCED_WS_RESERVED = 49152
+
+
 def balanced_workspace(B: int, Hq: int, Hkv: int, D: int, device):
-    """Device scratch for decode_paged_balanced (uint8 tensor, 256-byte aligned)."""
+    """Device scratch for decode_paged_balanced / decode_append / decode_paged_fp8 (uint8
+    tensor, 256-byte aligned, zero-filled: its leading counters must start at zero, and every
+    call leaves them zero, so the tensor can be reused across calls on one stream)."""
     n = int(load().gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def decode_paged_balanced(q, k_cache, v_cache, page_table, context_lens,

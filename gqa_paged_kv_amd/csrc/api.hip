@@ -72,7 +72,8 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
   if (ns == 1)
     return gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
                                     nullptr, B, Hq, Hkv, D, max_pages, 1, scale, dtype, s);
-  float* ws_o = (float*)data;
+  // the split partials start past the persistent path's counters, which stay zero
+  float* ws_o = (float*)(data + GQA_BALANCED_WS_RESERVED);
   float* ws_lse = ws_o + (size_t)B * Hq * ns * D;
   st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
                                 B, Hq, Hkv, D, max_pages, ns, scale, dtype, s);

@@ -10,19 +10,21 @@
 // "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
 // "核心参数调优：PackGQA与NumSplits的协同舞蹈") merged with the log-sum-exp rule.
 //
-// Two launches on the caller's stream. Items are ordered b-major, then kv head, then
-// page; N items in all, wave w of nw owns [N w / nw, N (w+1) / nw).
-//   1. balanced_kernel (persistent): every wave computes N and finds the sequence holding
-//      its first item with wave-wide scans of ceil(T_b / P). A unit wholly inside one
-//      share is finished and written directly; a cut unit leaves, per piece, a partial
-//      (normalised output + natural-log LSE) in the share's slot 0 (its first unit) or
-//      slot 1 (its last unit). Each wave keeps two pages in flight in VGPRs while it
-//      computes a third; all G <= 8 heads of the group live in the wave, so a K/V row is
-//      read once.
-//   2. fixup_kernel: one wave per (sequence, KV head) unit merges the pieces of cut units
-//      and zero-fills the rows of sequences with T_b = 0. (Merging inside the first
-//      kernel would need device-scope fences that write back and invalidate the L2 on
-//      every piece: measured slower than this second launch.)
+// One launch on the caller's stream. Items are ordered b-major, then kv head, then page;
+// N items in all, wave w of nw owns [N w / nw, N (w+1) / nw) (nw: the resident waves, fewer
+// for small batches so that a share holds at least kMinShare items). Every wave computes N
+// and finds the sequence holding its first item with wave-wide scans of ceil(T_b / P). A
+// unit wholly inside one share is finished and written directly; a cut unit leaves, per
+// piece, a partial (normalised output + natural-log LSE) in the share's slot 0 (its first
+// unit) or slot 1 (its last unit), written with device-coherent write-through stores of
+// whole 128-byte lines. After its last page a wave counts its pieces on per-group /
+// per-unit counters (device-scope atomics); the piece that completes a count merges (a
+// group of up to kGroup pieces, then the group partials of a long unit) and clears the
+// counter, so no second launch and no cache flush is needed. Each wave keeps pages in
+// flight in VGPRs while it computes one; all G <= 8 heads of the group live in the wave,
+// so a K/V row is read once. Rows of sequences with T_b = 0 are zero-filled.
+#include <atomic>
+
 #include "decode_common.h"
 #include "decode_mfma.h"
 
@@ -30,7 +32,26 @@ namespace gqa {
 
 constexpr int kBalancedMaxWaves = 4096;  // upper bound of the persistent grid (workspace size)
 
-// Workspace data region: kBalancedMaxWaves x 2 partial slots of G x (D + 1) floats.
+// Workspace: GQA_BALANCED_WS_RESERVED bytes of counters (kBalancedMaxWaves per-unit counters,
+// then 2 kBalancedMaxWaves per-group counters; zero between calls), then kBalancedMaxWaves x 2
+// partial slots of SlotGeom::FLOATS floats (whole 128-byte lines).
+constexpr int kGroup = 8;  // pieces merged together at the first level
+static_assert(GQA_BALANCED_WS_RESERVED == 3 * kBalancedMaxWaves * 4, "counter region");
+
+// Partial slot of one piece: the G x D normalised output as 16-byte chunks, chunk i * 64 +
+// lane holding pair k = 4 i + lane / 16 (head k / JPH, chunk k % JPH of that head's E dims
+// of the lane's row-column lane % 16: dims lane_dim(lane % 16, 4 (k % JPH)) .. + 3), then the
+// G natural-log LSEs. Every lane of a wave stores and loads 16 contiguous bytes, so each
+// wave instruction moves whole 128-byte lines (the stores are write-through, device-coherent).
+template <int G, int D>
+struct SlotGeom {
+  static constexpr int JPH = D / 64;  // 4-float chunks per head per row-column
+  static constexpr int NK = G * JPH;  // (head, chunk) pairs per row-column
+  static constexpr int NI = (NK + 3) / 4;
+  static constexpr int DATA = G * D;
+  static constexpr int FLOATS = (G * D + G + 31) / 32 * 32;
+};
+constexpr int kSc1 = 16;  // cache-policy bit of the buffer builtins: device-scope (sc1)
 
 // Tokens attended by sequence b: T_b clamped to [0, max_pages * P]; with append = 1 (the
 // step's own token is appended at position T_b first) T_b is clamped to
@@ -94,21 +115,195 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ context_
   }
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* slots, int G, int D) {
+  const int floats = (G * D + G + 31) / 32 * 32;
+  return __builtin_amdgcn_make_buffer_rsrc(slots, 0, (int)(kBalancedMaxWaves * 2 * floats * 4),
+                                           0x00020000);
+}
+__device__ __forceinline__ f32x4_t load_sc1(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kSc1));
+}
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, kSc1);
+}
+
+// This wave's piece (acc[h] x inv[h], natural-log LSEs lse[h]) into the slot at byte `off`.
+// After merge_rows every row of the wave holds the same data, so the four rows store
+// different (head, chunk) pairs.
+template <int D, int G, typename WS>
+__device__ __forceinline__ void store_piece(__amdgpu_buffer_rsrc_t rs, uint32_t off, const WS& st,
+                                            const float (&inv)[G], const float (&lse)[G],
+                                            int lane) {
+  using SG = SlotGeom<G, D>;
+  const int r = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < SG::NI; ++i) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int k = 4 * i + rr;
+      if (k < SG::NK && r == rr) {
+        const int h = k / SG::JPH, j = k % SG::JPH;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) v[kk] = st.acc[h][4 * j + kk] * inv[h];
+      }
+    }
+    if (4 * i + r < SG::NK) store_sc1(rs, off + (uint32_t)(i * kWave + lane) * 16, v);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int q4 = 0; q4 < (G + 3) / 4; ++q4) {
+      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (4 * q4 + kk < G) v[kk] = lse[4 * q4 + kk];
+      store_sc1(rs, off + (uint32_t)(SG::DATA + 4 * q4) * 4, v);
+    }
+  }
+}
+
+// Merge `count` pieces (slot byte offsets off_of(p)) with the log-sum-exp rule. TO_OUT: write
+// the G output rows at dst_row (bf16 / fp32); otherwise write a merged partial (same slot
+// layout) at byte dst_off. Lane p holds piece p's LSEs; the pieces' data are read KB at a time.
+template <typename T, int D, int G, bool TO_OUT, typename OffFn>
+__device__ __forceinline__ void merge_pieces(__amdgpu_buffer_rsrc_t rs, int count, OffFn off_of,
+                                             T* __restrict__ dst_row, uint32_t dst_off,
+                                             int lane) {
+  using SG = SlotGeom<G, D>;
+  constexpr int NL = (G + 3) / 4;
+  constexpr int KB = 8;
+  const int r = lane >> 4;
+  const int qd = lane & 15;
+  float m_run[G], den[G];
+  f32x4_t num[SG::NI];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    den[h] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < SG::NI; ++i) num[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the weight of this lane's head in slot chunk i, from per-head values
+  auto lane_head_value = [&](const float (&vh)[G], int i) {
+    float x = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int k = 4 * i + rr;
+      if (k < SG::NK && r == rr) x = vh[k / SG::JPH];
+    }
+    return x;
+  };
+  for (int c0 = 0; c0 < count; c0 += kWave) {
+    const int n_c = min(kWave, count - c0);
+    const bool live = lane < n_c;
+    float lse[G];
+    {
+      const uint32_t lo = off_of(c0 + (live ? lane : 0)) + SG::DATA * 4;
+#pragma unroll
+      for (int q4 = 0; q4 < NL; ++q4) {
+        const f32x4_t x = load_sc1(rs, lo + 16 * q4);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          if (4 * q4 + kk < G) lse[4 * q4 + kk] = x[kk];
+      }
+    }
+    // the first batch of pieces' data, issued with the LSE loads (it does not depend on them)
+    f32x4_t x[KB][SG::NI];
+    auto load_batch = [&](int p0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint32_t po = off_of(c0 + min(p0 + kb, n_c - 1));
+#pragma unroll
+        for (int i = 0; i < SG::NI; ++i)
+          x[kb][i] = 4 * i + r < SG::NK ? load_sc1(rs, po + (uint32_t)(i * kWave + lane) * 16)
+                                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    load_batch(0);
+    float w[G], resc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float M = live ? lse[h] : -INFINITY;
+      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      M = fmaxf(M, m_run[h]);
+      resc[h] = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[h] - M) * kLog2e);
+      w[h] = live ? __builtin_amdgcn_exp2f((lse[h] - M) * kLog2e) : 0.f;
+      float ws = w[h];
+      for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+      den[h] = den[h] * resc[h] + ws;
+      m_run[h] = M;
+    }
+#pragma unroll
+    for (int i = 0; i < SG::NI; ++i) num[i] *= lane_head_value(resc, i);
+    for (int p0 = 0;;) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (p0 + kb < n_c) {
+          float wu[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            wu[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[h]), p0 + kb));
+#pragma unroll
+          for (int i = 0; i < SG::NI; ++i) num[i] += lane_head_value(wu, i) * x[kb][i];
+        }
+      }
+      p0 += KB;
+      if (p0 >= n_c) break;
+      load_batch(p0);
+    }
+  }
+  float inv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) inv[h] = 1.0f / den[h];
+#pragma unroll
+  for (int i = 0; i < SG::NI; ++i) {
+    const f32x4_t o = num[i] * lane_head_value(inv, i);
+    if constexpr (TO_OUT) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int k = 4 * i + rr;
+        if (k < SG::NK && r == rr) {
+          T* dst = dst_row + (k / SG::JPH) * D + lane_dim<T, D>(qd, 4 * (k % SG::JPH));
+          if constexpr (sizeof(T) == 2) {
+            *(u32x2_t*)dst = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          } else {
+            *(f32x4_t*)dst = o;
+          }
+        }
+      }
+    } else {
+      if (4 * i + r < SG::NK) store_sc1(rs, dst_off + (uint32_t)(i * kWave + lane) * 16, o);
+    }
+  }
+  if constexpr (!TO_OUT) {
+    if (lane == 0) {
+#pragma unroll
+      for (int q4 = 0; q4 < NL; ++q4) {
+        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          if (4 * q4 + kk < G) v[kk] = m_run[4 * q4 + kk] + __builtin_log2f(den[4 * q4 + kk]) * kLn2;
+        store_sc1(rs, dst_off + (uint32_t)(SG::DATA + 4 * q4) * 4, v);
+      }
+    }
+  }
+}
+
 // T: q / out element type; TKV: cache element type (T, or an 8-bit float whose per-tensor
 // scales are folded in: k_scale into scale_log2, v_scale into out_scale).
 template <typename T, int D, int G, typename TKV = T, bool APPEND = false>
 __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     const T* __restrict__ q, const TKV* __restrict__ k_cache, const TKV* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ context_lens,
-    T* __restrict__ out, float* __restrict__ slots, int B, int Hq, int Hkv, int max_pages,
-    float scale_log2, float out_scale, const TKV* __restrict__ k_new,
+    T* __restrict__ out, float* __restrict__ slots, int* __restrict__ counters, int B, int Hq,
+    int Hkv, int max_pages, float scale_log2, float out_scale, const TKV* __restrict__ k_new,
     const TKV* __restrict__ v_new, TKV* __restrict__ k_store, TKV* __restrict__ v_store) {
   using S = DecodeShape<TKV, D, G>;
   constexpr int append = APPEND ? 1 : 0;
   static_assert(S::HG == 1, "all heads of the group in one wave");
   constexpr int W32 = S::W32;
   constexpr int E = S::E;
-  constexpr int SLOT = G * (D + 1);
+  using SG = SlotGeom<G, D>;
 
   const int lane = lane_id();
   const int r = lane >> 4;
@@ -122,6 +317,15 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     part += pages_of(context_lens, bb, max_pages, append);
   const long N = uniform((long)Hkv * wave_sum(part));
 
+  if constexpr (!APPEND) {  // T_b = 0: the output rows are zero (one wave per sequence)
+    for (int bb = gw; bb < B; bb += (int)gridDim.x * kDecodeWaves) {
+      if (pages_of(context_lens, bb, max_pages, 0) != 0) continue;
+      T* zrow = out + (size_t)bb * Hq * D;
+      for (int x = lane; x < Hq * D; x += kWave) {
+        if constexpr (sizeof(T) == 2) ((uint16_t*)zrow)[x] = 0; else zrow[x] = 0.f;
+      }
+    }
+  }
   if (N == 0) return;
   const int nw = active_waves(N, gridDim.x * kDecodeWaves);
   if (gw >= nw) return;  // no share: items [N gw / nw, ...) would lie past the last item
@@ -211,8 +415,21 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     }
   };
 
+  // Pieces of cut units held by this share (at most one per slot), published at its end.
+  struct Piece {
+    long first;  // first item of the unit
+    int np;      // the unit's item count
+    int valid;
+    size_t dst;  // output row offset of the unit
+  };
+  Piece piece0{0, 0, 0, 0}, piece1{0, 0, 0, 0};
+  const __amdgpu_buffer_rsrc_t rs = slot_rsrc(slots, G, D);
+  auto slot_off = [&](int w, int sl) {
+    return (uint32_t)(((size_t)w * 2 + sl) * SG::FLOATS * 4);
+  };
+
   // Finish the segment that ends at item i: merge the 4 DPP rows, then write the output
-  // (the whole unit is in this share) or the piece's partial.
+  // (the whole unit is in this share) or the piece's partial (write-through stores).
   auto finish = [&](long i) {
     st.merge_rows();
     const long first = i - pg;  // first item of the unit (pg = page of item i)
@@ -223,16 +440,16 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
       return;
     }
     const int slot = seg_start == lo ? 0 : 1;
-    float* base = slots + ((size_t)gw * 2 + slot) * SLOT;
+    float inv[G], lse[G];
 #pragma unroll
     for (int hw = 0; hw < G; ++hw) {
-      const float inv = out_scale / st.l[hw];
-      if (r == 0) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) base[hw * (D + 1) + lane_dim<T, D>(qd, e)] = st.acc[hw][e] * inv;
-      }
-      if (lane == 0) base[hw * (D + 1) + D] = (st.m[hw] + __builtin_log2f(st.l[hw])) * kLn2;
+      inv[hw] = out_scale / st.l[hw];
+      lse[hw] = (st.m[hw] + __builtin_log2f(st.l[hw])) * kLn2;
     }
+    store_piece<D, G>(rs, slot_off(gw, slot), st, inv, lse, lane);
+    const Piece pc{uniform(first), uniform(np), 1,
+                   (size_t)uniform((long)(((size_t)b * Hq + kvh * G) * D))};
+    if (slot == 0) piece0 = pc; else piece1 = pc;
   };
 
   // Consume item i from buffer `buf`, then move the compute cursor; open a new segment
@@ -289,113 +506,54 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
       if (i + k + 1 >= hi) break;
     }
   }
-}
 
-// ---- fix-up: merge the pieces of cut units; zero rows of empty sequences ----------------
-// One wave per (sequence, KV head, query head of the group). Lane p holds piece p's LSE;
-// the weights come from wave reductions; each lane then sums its D / 64 dims over the
-// pieces, KB pieces per batch, the first batch's loads issued together with the LSE loads
-// (they do not depend on them), so a unit cut into up to KB pieces costs one memory round
-// trip after the page-count scan. Pieces are taken 64 at a time.
-constexpr int kFixupWaves = 4;
-
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kFixupWaves * kWave) void fixup_kernel(
-    const float* __restrict__ slots, const int32_t* __restrict__ context_lens,
-    T* __restrict__ out, int B, int Hq, int Hkv, int max_pages, int nw, int append) {
-  constexpr int SLOT = G * (D + 1);
-  constexpr int DL = D / kWave;  // dims per lane
-  constexpr int KB = 32;         // pieces per batch
-  const int lane = lane_id();
-  const long t = (long)blockIdx.x * kFixupWaves + wave_id();
-  if (t >= (long)B * Hkv * G) return;
-  const long u = t / G;  // (sequence, KV head) unit
-  const int hl = (int)(t % G);
-  const int b = (int)(u / Hkv);
-  const int kvh = (int)(u % Hkv);
-  // N and the first item of sequence b in one pass over the page counts
-  long part_all = 0, part_before = 0;
-  for (int bb = lane; bb < B; bb += kWave) {
-    const int n = pages_of(context_lens, bb, max_pages, append);
-    part_all += n;
-    part_before += bb < b ? n : 0;
-  }
-  const long N = (long)Hkv * wave_sum(part_all);
-  nw = active_waves(N, nw);
-  const int np = pages_of(context_lens, b, max_pages, append);
-  T* dst = out + ((size_t)b * Hq + kvh * G + hl) * D;
-  if (np == 0) {  // T_b == 0: the output is zero
-#pragma unroll
-    for (int j = 0; j < DL; ++j) {
-      if constexpr (sizeof(T) == 2) ((uint16_t*)dst)[lane + kWave * j] = 0;
-      else dst[lane + kWave * j] = 0.f;
+  // Publish the pieces. The wait covers this wave's partial stores; only then is a piece
+  // counted. Units of up to kGroup pieces: the piece that completes its group's count
+  // merges the unit into the output. Longer units: the last piece of each group of kGroup
+  // consecutive pieces merges the group into a partial (in the group's first slot) and
+  // counts it on the unit's counter; the last group merges the group partials. Whoever
+  // completes a count clears that counter for the next call.
+  if ((piece0.valid | piece1.valid) == 0) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int* const unit_cnt = counters;
+  int* const group_cnt = counters + kBalancedMaxWaves;
+  auto count_in = [&](int* c) {
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = uniform(old);
+    asm volatile("" ::: "memory");
+    return old + 1;
+  };
+  auto clear = [&](int* c) {
+    if (lane == 0) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto publish = [&](const Piece& pc) {
+    const int w0 = share_owner(N, pc.first, nw);
+    const int w1 = share_owner(N, pc.first + pc.np - 1, nw);
+    const int npc = w1 - w0 + 1;                                   // pieces of the unit
+    const int s0 = share_lo(N, w0, nw) == pc.first ? 0 : 1;        // slot of piece 0
+    const int g = (gw - w0) / kGroup;
+    const int gfirst = w0 + g * kGroup;
+    const int gsize = min(kGroup, npc - g * kGroup);
+    const int ngroups = (npc + kGroup - 1) / kGroup;
+    int* gc = group_cnt + 2 * gfirst + (g == 0 ? s0 : 0);
+    if (count_in(gc) != gsize) return;  // another piece of the group is still running
+    clear(gc);
+    auto piece_off = [&](int p) { return slot_off(gfirst + p, (g == 0 && p == 0) ? s0 : 0); };
+    if (ngroups == 1) {
+      merge_pieces<T, D, G, true>(rs, gsize, piece_off, out + pc.dst, 0u, lane);
+      return;
     }
-    return;
-  }
-  const long first = (long)Hkv * wave_sum(part_before) + (long)kvh * np;
-  const int w0 = share_owner(N, first, nw);
-  const int w1 = share_owner(N, first + np - 1, nw);
-  if (w0 == w1) return;  // finished and written by its wave
-  const bool head_is_first = share_lo(N, w0, nw) == first;
-
-  float m_run = -INFINITY, den = 0.f, num[DL];
-#pragma unroll
-  for (int j = 0; j < DL; ++j) num[j] = 0.f;
-  float v[KB][DL];
-  for (int c0 = w0; c0 <= w1; c0 += kWave) {
-    const int np_c = min(kWave, w1 - c0 + 1);
-    // lane p: piece c0 + p (empty shares wrote nothing: weight 0, slot never used)
-    const int w = c0 + lane;
-    const bool live = lane < np_c && share_lo(N, w, nw) != share_lo(N, w + 1, nw);
-    const int slot = (w == w0 && !head_is_first) ? 1 : 0;
-    const int off = live ? (int)(((size_t)w * 2 + slot) * SLOT) + hl * (D + 1) : 0;
-    const float lse = slots[off + D];
-    // data of KB pieces; dead pieces read a valid slot and are replaced by zero
-    auto load_batch = [&](int p0) {
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int p = (p0 + k) & (kWave - 1);
-        const int po = __builtin_amdgcn_readlane(off, p);
-        const bool pl = p0 + k < np_c && __builtin_amdgcn_readlane((int)live, p) != 0;
-#pragma unroll
-        for (int j = 0; j < DL; ++j) {
-          const float x = slots[po + lane + kWave * j];
-          v[k][j] = pl ? x : 0.f;
-        }
-      }
-    };
-    load_batch(0);
-    float M = live ? lse : -INFINITY;
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    M = fmaxf(M, m_run);
-    const float rescale = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * kLog2e);
-    const float wgt = live ? __builtin_amdgcn_exp2f((lse - M) * kLog2e) : 0.f;
-    float ws = wgt;
-    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
-    den = den * rescale + ws;
-#pragma unroll
-    for (int j = 0; j < DL; ++j) num[j] *= rescale;
-    m_run = M;
-    for (int p0 = 0;;) {
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const float wv = __builtin_amdgcn_readlane(__float_as_int(wgt), (p0 + k) & (kWave - 1));
-#pragma unroll
-        for (int j = 0; j < DL; ++j) num[j] = fmaf(__int_as_float(wv), v[k][j], num[j]);
-      }
-      p0 += KB;
-      if (p0 >= np_c) break;
-      load_batch(p0);
-    }
-  }
-  const float inv = 1.0f / den;
-#pragma unroll
-  for (int j = 0; j < DL; ++j) {
-    const float o = num[j] * inv;
-    const int d = lane + kWave * j;
-    if constexpr (sizeof(T) == 2) ((uint16_t*)dst)[d] = f32_to_bf16(o);
-    else dst[d] = o;
-  }
+    merge_pieces<T, D, G, false>(rs, gsize, piece_off, out, piece_off(0), lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int* uc = unit_cnt + w0;
+    if (count_in(uc) != ngroups) return;
+    clear(uc);
+    auto group_off = [&](int gg) { return slot_off(w0 + gg * kGroup, gg == 0 ? s0 : 0); };
+    merge_pieces<T, D, G, true>(rs, ngroups, group_off, out + pc.dst, 0u, lane);
+  };
+  if (piece0.valid) publish(piece0);
+  if (piece1.valid) publish(piece1);
 }
 
 // ---- host side --------------------------------------------------------------------------
@@ -408,11 +566,11 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
                            const void* v_new = nullptr, void* k_store = nullptr,
                            void* v_store = nullptr) {
   // Persistent grid = resident workgroups; a per-device cache of an occupancy query
-  // (every thread computes and stores the same value).
-  static int grid_cache[64] = {0};
+  // (threads that race on a first call all compute and store the same value).
+  static std::atomic<int> grid_cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GQA_ERR_LAUNCH;
-  int grid = grid_cache[dev];
+  int grid = grid_cache[dev].load(std::memory_order_relaxed);
   if (grid == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -422,17 +580,14 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
       return GQA_ERR_LAUNCH;
     grid = cus * (per_cu > 0 ? per_cu : 1);
     if (grid * kDecodeWaves > kBalancedMaxWaves) grid = kBalancedMaxWaves / kDecodeWaves;
-    grid_cache[dev] = grid;
+    grid_cache[dev].store(grid, std::memory_order_relaxed);
   }
-  float* slots = (float*)slots_ws;
+  int* counters = (int*)slots_ws;
+  float* slots = (float*)((char*)slots_ws + GQA_BALANCED_WS_RESERVED);
   hipLaunchKernelGGL((balanced_kernel<T, D, G, TKV, APPEND>), dim3(grid), dim3(kDecodeThreads), 0, s,
-                     (const T*)q, (const TKV*)k, (const TKV*)v, pt, lens, (T*)out, slots, B, Hq,
-                     Hkv, max_pages, scale * kLog2e, out_scale, (const TKV*)k_new,
+                     (const T*)q, (const TKV*)k, (const TKV*)v, pt, lens, (T*)out, slots, counters,
+                     B, Hq, Hkv, max_pages, scale * kLog2e, out_scale, (const TKV*)k_new,
                      (const TKV*)v_new, (TKV*)k_store, (TKV*)v_store);
-  const unsigned fix_grid = (unsigned)(((long)B * Hq + kFixupWaves - 1) / kFixupWaves);
-  hipLaunchKernelGGL((fixup_kernel<T, D, G>), dim3(fix_grid), dim3(kFixupWaves * kWave), 0, s,
-                     slots, lens, (T*)out, B, Hq, Hkv, max_pages, grid * kDecodeWaves,
-                     APPEND ? 1 : 0);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 

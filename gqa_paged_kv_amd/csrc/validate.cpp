@@ -93,10 +93,13 @@ int gqa_balanced_auto_splits(int B, int Hkv) {
 size_t gqa_decode_balanced_workspace_bytes(int B, int Hq, int Hkv, int D) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
   const size_t G = (size_t)(Hq / Hkv);
-  // persistent path: 4096 waves x 2 slots x G x (D + 1) floats
-  const size_t slot_bytes = (size_t)4096 * 2 * G * (D + 1) * sizeof(float);
-  const size_t split_bytes = gqa_decode_workspace_bytes(B, Hq, D, gqa_balanced_auto_splits(B, Hkv));
-  return slot_bytes > split_bytes ? slot_bytes : split_bytes;
+  // counters (zero between calls), then either the persistent path's 4096 waves x 2 slots
+  // of G x D + G floats rounded up to whole 128-byte lines, or the split path's partials
+  const size_t slot_floats = (G * D + G + 31) / 32 * 32;
+  const size_t slot_bytes = G <= 8 ? (size_t)4096 * 2 * slot_floats * sizeof(float) : 0;
+  const size_t split_bytes =
+      G >= 16 ? gqa_decode_workspace_bytes(B, Hq, D, gqa_balanced_auto_splits(B, Hkv)) : 0;
+  return GQA_BALANCED_WS_RESERVED + (slot_bytes > split_bytes ? slot_bytes : split_bytes);
 }
 
 int gqa_validate_prefill(const void* q, const void* k, const void* v, const void* k_cache,

@@ -54,6 +54,10 @@ typedef enum {
   GQA_ERR_LAUNCH = 3       /* the HIP runtime refused the kernel launch */
 } gqa_status;
 
+/* Bytes at the start of a balanced-decode workspace that hold counters: they must be zero
+ * before the first call that uses the workspace, and every call leaves them zero. */
+#define GQA_BALANCED_WS_RESERVED 49152
+
 typedef enum {
   GQA_F32 = 0,
   GQA_BF16 = 1,
@@ -106,10 +110,14 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *
  *   workspace        device scratch of at least
  *                    gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D) bytes, 256-byte
- *                    aligned, owned by the caller; no initialisation needed, contents are
- *                    overwritten. Calls that share a workspace must not overlap in time.
+ *                    aligned, owned by the caller. Zero it once after allocating it: its
+ *                    first GQA_BALANCED_WS_RESERVED bytes are counters that every call
+ *                    leaves at zero (the rest is overwritten). One workspace serves every
+ *                    shape whose size it covers. Calls that share a workspace must not
+ *                    overlap in time.
  *   other arguments  as for gqa_decode_paged.
- * Enqueues two kernels on `stream` (decode + fix-up; for G >= 16 split decode + combine).
+ * Enqueues one kernel on `stream` for G <= 8 (the pieces of units cut by the partition are
+ * merged by the piece that finishes last); for G >= 16 the split decode + combine.
  */
 int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* page_table, const int32_t* context_lens, void* out,
@@ -136,7 +144,7 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
  *   out          [B][Hq][D]    dtype
  *   workspace    as for gqa_decode_paged_balanced
  * Supported: D in {64, 128}, P = 16, G in {1, 2, 4, 8}, dtype GQA_F32 or GQA_BF16.
- * Enqueues two kernels (decode with the append folded in + fix-up).
+ * Enqueues one kernel (decode with the append folded in).
  */
 int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
                       void* v_cache, const int32_t* page_table, const int32_t* context_lens,
@@ -160,7 +168,7 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
  *   out          [B][Hq][D]              bf16 (round to nearest even)
  *   workspace    as for gqa_decode_paged_balanced (same size function)
  *   other arguments as for gqa_decode_paged_balanced.
- * Supported: D = 128, G in {1, 2, 4, 8}, P = 16. Enqueues two kernels (decode + fix-up).
+ * Supported: D = 128, G in {1, 2, 4, 8}, P = 16. Enqueues one kernel.
  */
 int gqa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale,
                          float v_scale, const int32_t* page_table, const int32_t* context_lens,

@@ -58,6 +58,22 @@ def test_workspace_bytes(lib):
     assert g.workspace_bytes(0, 32, 128, 16) == 0
 
 
+def test_balanced_workspace_layout(lib):
+    """The counter region the header reserves at the start of a balanced-decode workspace is
+    the one the binding knows, and the size function adds it to the larger of the persistent
+    path's slots (whole 128-byte lines per piece) and the split path's partials."""
+    text = open(os.path.join(ROOT, "include", "gqa.h")).read()
+    m = re.search(r"#define\s+GQA_BALANCED_WS_RESERVED\s+(\d+)", text)
+    assert m and int(m.group(1)) == g.BALANCED_WS_RESERVED == 3 * 4096 * 4
+    n = lib.gqa_decode_balanced_workspace_bytes
+    slot_floats = (4 * 128 + 4 + 31) // 32 * 32  # G = 4, D = 128
+    assert n(64, 32, 8, 128) == g.BALANCED_WS_RESERVED + 4096 * 2 * slot_floats * 4
+    assert n(64, 32, 8, 128) % 256 == 0
+    assert n(0, 32, 8, 128) == 0 and n(4, 30, 8, 128) == 0
+    # G >= 16 takes the split path: counters, then its partials only
+    assert n(8, 32, 1, 128) == g.BALANCED_WS_RESERVED + g.workspace_bytes(8, 32, 128, 16)  # NS = 16
+
+
 def _vd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, pt=FAKE, lens=FAKE, out=FAKE, wo=None, wl=None, B=2, Hq=8,
              Hkv=2, D=128, P=16, max_pages=4, num_pages=8, ns=1, scale=0.125, dtype=g.BF16)

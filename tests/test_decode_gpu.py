@@ -343,12 +343,11 @@ def test_balanced_all_sequences_empty_and_clamped_lengths(gpu_lib):
 
 
 def test_balanced_workspace_reused_across_shapes(gpu_lib):
-    """One workspace serves a run of calls with different head shapes and length mixes (units
-    cut into 2 pieces, into hundreds of pieces, empty sequences, the G >= 16 split path in
-    between): every result matches the oracle and rows of empty sequences are written as
-    zeros over a NaN-filled output."""
+    """One zero-filled workspace serves a run of calls with different head shapes and length
+    mixes (units cut into 2 pieces, into hundreds of pieces, empty sequences, the G >= 16 split
+    path in between): every result matches the oracle, rows of empty sequences are written as
+    zeros over a NaN-filled output, and the leading counters are zero again after every call."""
     import gqa_paged_kv_amd as gk
-    ws = gk.balanced_workspace(64, 32, 1, 128, DEV)  # the largest shape below (G = 32)
     cases = [
         ("bf16", 32, 8, [37, 300, 16, 0, 1000, 5, 0, 64]),
         ("bf16", 32, 8, [4096]),          # one sequence: each unit cut into many pieces
@@ -357,6 +356,9 @@ def test_balanced_workspace_reused_across_shapes(gpu_lib):
         ("bf16", 8, 8, [2000, 0, 999]),   # G = 1
         ("bf16", 32, 8, [37, 300, 16, 0, 1000, 5, 0, 64]),
     ]
+    size = max(int(gk.load().gqa_decode_balanced_workspace_bytes(len(lens), hq, hkv, 128))
+               for (_, hq, hkv, lens) in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device=DEV)
     for i, (dtype, hq, hkv, lens) in enumerate(cases):
         print(f"[balanced] workspace reuse {i} {dtype} {hq}x{hkv} B={len(lens)}", flush=True)
         x = synth.decode_inputs(len(lens), hq, hkv, 128, 16, lens, dtype, seed=500 + i,
@@ -369,6 +371,7 @@ def test_balanced_workspace_reused_across_shapes(gpu_lib):
         for b, t in enumerate(lens):
             if t == 0:
                 assert torch.all(out[b] == 0), f"case {i}: empty sequence {b} not zeroed"
+        assert torch.all(ws[:gk.BALANCED_WS_RESERVED] == 0), f"case {i}: counters left non-zero"
 
 
 # ---------------------------------------------------------------- scale sign and magnitude
