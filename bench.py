@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the paged GQA hot path on one MI355X.
 
-A step is one pass of the decode path (balanced decode kernel + fix-up merge,
-``gqa_decode_paged_balanced``; ``--splits NS`` times the split path instead) over
+A step is one pass of the decode path (the balanced decode kernel, which also
+merges the units it cut, ``gqa_decode_paged_balanced``; ``--splits NS`` times the
+split path instead) over
 the paged-decode workload: B=64 sequences, Hq=32, Hkv=8, D=128, page 16, context
 lengths uniform in [512, 4096], bf16, pages scattered by a seeded
 permutation. Inputs are resident in HBM before the timed region. ``value`` is
@@ -252,7 +253,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode_balanced_bf16_B64_Hq32_Hkv8") if ns == 0 else None,
             "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, calibrated)",
-            "kernel": ("balanced_kernel<bf16,128,4> + fixup_kernel (one decode call)" if ns == 0
+            "kernel": ("balanced_kernel<bf16,128,4> (one decode call, one launch)" if ns == 0
                        else "decode_regs_kernel<bf16,128,4> + combine_kernel (one decode call)"),
             "event_avg_us": round(ev_avg * 1e3, 2),
             "event_per_call_us": round(ev_call * 1e3, 2),
@@ -292,7 +293,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(f8gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(f8gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode_balanced_fp8e4m3_B64_Hq32_Hkv8"),
-                         "kernel": "balanced_kernel<bf16,128,4,fp8e4m3> + fixup_kernel"},
+                         "kernel": "balanced_kernel<bf16,128,4,fp8e4m3> (one launch)"},
         }
         del f8, f8out, f8ws
 

@@ -314,7 +314,7 @@ def test_balanced_config5(gpu_lib, B, Hkv):
                                          (1, 4, 1, 16), (3, 32, 8, 40)])
 def test_balanced_small_batches_use_fewer_waves(gpu_lib, B, hq, hkv, T):
     """Batches with fewer than a few pages per resident wave: only N / 4 waves take a share
-    (the others must return at once) and the fix-up uses the same partition."""
+    (the others must return at once) and the merge of cut units uses the same partition."""
     print(f"[balanced] small batch B={B} {hq}x{hkv} T={T}", flush=True)
     x = synth.decode_inputs(B, hq, hkv, 128, 16, [T] * B, "bf16", seed=B * 31 + T, device=DEV)
     assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"small batch B={B} T={T}")
