@@ -8,16 +8,19 @@
 // memory and only the output is written (page "TensorRT-LLM与TensorRT核心差异解析",
 // section 4.2.1).
 //
-// Work decomposition: one workgroup (8 waves) per (b, kvh, q-tile). The q-tile holds
+// Work decomposition: the unit of work (an item) is a (b, kvh, q-tile). The q-tile holds
 // 256 query rows: all G heads of the group x 256/G positions (the G heads are packed
 // into one workgroup so that every K/V tile is staged in LDS once and read by all of
-// them). Wave w owns 32 rows: one head, 32 consecutive positions. Workgroups are
-// issued heaviest (last) q-tile first; blockIdx.x runs over (b, kvh) so all q-tiles
-// of one (b, kvh) land on the same XCD and share its L2.
+// them). Wave w of the 8 owns 32 rows: one head, 32 consecutive positions. The kernel is
+// persistent: one workgroup per compute unit serves one (b, kvh) and walks a list of its
+// q-tiles (schedule at the kernel), so that a workgroup's start-up (Q rows, first key
+// tile) and its stores overlap work instead of leaving the compute unit idle between
+// workgroups.
 //
 // Per 64-key tile and wave (all on-chip):
 //   S^T = K Q^T   16 MFMAs; A = K rows from LDS (ds_read_b128, XOR-swizzled rows),
-//                 B = Q^T held in registers for the whole kernel.
+//                 B = Q^T held in registers for the whole item (read from LDS, where
+//                 the previous item fetched it).
 //   softmax       S^T's C layout gives every lane 32 scores of ONE query, so the row
 //                 max / sum are lane-local plus one exchange between the two half-waves;
 //                 exp2 with scale*log2(e) folded in; the running max is only raised when
@@ -25,6 +28,8 @@
 //   O^T += V^T P^T 16 MFMAs; A = V^T read straight from the key-major V tile with
 //                 ds_read_b64_tr_b16 (no transpose pass), B = P^T from registers (bf16).
 // K/V tiles stream HBM -> LDS with global_load_lds_dwordx4, double-buffered.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -60,6 +65,23 @@ __device__ __forceinline__ void buffer_dma16(u32x4_t rsrc, uint32_t voffset, uin
                : "memory");
 }
 
+// 4 bytes per lane from a raw buffer into LDS (LDS address M0 + 4 * lane); same ordering
+// rules as buffer_dma16.
+__device__ __forceinline__ void buffer_dma4(u32x4_t rsrc, uint32_t voffset, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
+// The lane index, computed afresh (v_mbcnt) where it is used: the asm statement cannot be
+// hoisted, so the compiler neither keeps it nor values derived from it live across loops.
+__device__ __forceinline__ int fresh_lane() {
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  return ln;
+}
+
 // Raw buffer descriptor: 48-bit base, stride 0, num_records bytes, gfx9 data format word.
 __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t num_records) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
@@ -74,32 +96,43 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t num_reco
 // PAGED = true: chunked prefill. Sequence b already holds past_lens[b] tokens in the cache
 // and its new_lens[b] new tokens (already appended by append_at_kernel) sit at positions
 // past .. past+new-1; new row i attends keys 0 .. past+i, all read from the paged cache.
+//
+// Persistent schedule: workgroup g serves the (b, kv head) pair c = g % nbkv and walks a
+// list of its q-tiles (items). With A = rows_per_round workgroups per pair, round r gives
+// workgroup row a = g / nbkv the q-tile of rank r * A + a (r even) or r * A + A - 1 - a
+// (r odd), rank 0 being the last, heaviest q-tile: the causal triangle is dealt out in a
+// snake so that every workgroup gets a near-equal number of key tiles, and all q-tiles of
+// one pair run on the XCD of its workgroups (workgroup g runs on XCD g % 8, and c % 8 ==
+// g % 8 when 8 divides nbkv) and share its L2. Between two items the workgroup does not
+// drain: the next item's Q rows are fetched into LDS while the current item still runs,
+// and its output is stored after the next item has started.
 template <int G, bool PAGED>
 __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_causal_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ out, bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ past_lens,
     const int32_t* __restrict__ new_lens, int max_pages, int S, int Hq, int Hkv,
-    float scale_log2, int n_qtiles) {
+    float scale_log2, int n_qtiles, int nbkv, int rows_per_round) {
   using namespace prefill;
   constexpr int BMPOS = 256 / G;  // positions per q-tile
   constexpr int PB = 8 / G;       // 32-position blocks per head
 
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];  // [stage][K, V]
+  // LDS: [stage][K, V] tiles (64 KiB); K tile 0, loaded once (16 KiB: every item of the
+  // workgroup has the same (b, kv head), hence the same first key tile); the Q rows of
+  // the next item, 8 KiB per wave (64 KiB); the current item's page ids, 256 bytes per wave
+  // (causal prefill: used by the KV append).
+  constexpr uint32_t K0_OFF = 2 * 2 * TILE;
+  constexpr uint32_t Q_OFF = K0_OFF + TILE;
+  constexpr uint32_t PT_OFF = Q_OFF + WAVES * 32 * ROWB;
+  __shared__ __attribute__((aligned(16))) char smem[PT_OFF + WAVES * 256];
 
-  const int bkv = blockIdx.x;
+  const int bkv = (int)blockIdx.x % nbkv;
+  const int arow = (int)blockIdx.x / nbkv;
   const int b = bkv / Hkv;
   const int kvh = bkv % Hkv;
-  const int qt = n_qtiles - 1 - (int)blockIdx.y;
-  const int q0 = qt * BMPOS;
   const int w = wave_id();
-  const int lane = lane_id();
-  const int l32 = lane & 31;
-  const int half = lane >> 5;
   const int hl = w / PB;
   const int h = kvh * G + hl;
-  const int qa = q0 + 32 * (w % PB);  // first new row of this wave
-  const int my_q = qa + l32;          // the new row this lane's softmax state belongs to
 
   // p: tokens already cached before this call's rows, n: live new rows (lengths clamped
   // to what the page table row can address)
@@ -108,43 +141,53 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     const int cap = max_pages * 16;
     p = min(max(past_lens[b], 0), cap);
     n = min(max(new_lens[b], 0), min(S, cap - p));
-    if (q0 >= n) return;  // the whole workgroup: no live row (before any barrier)
   }
   const int end = p + n;  // keys of the sequence after this call
-  const int my_pos = p + my_q;  // absolute position of this lane's query
-  const int wave_tiles = qa < n ? (p + min(qa + 31, n - 1)) / BN + 1 : 0;
-  const int wg_tiles = (p + min(q0 + BMPOS, n) - 1) / BN + 1;
-  const int mask_from = (p + qa) / BN;  // tiles before it are below every row of the wave
+  // q-tile of round r (-1 past the last round), and the next round after r whose q-tile
+  // holds a live row (-1 if none): a short chunk leaves the heaviest q-tiles empty
+  auto qt_of = [&](int r) {
+    const int rank = r * rows_per_round + ((r & 1) ? rows_per_round - 1 - arow : arow);
+    return rank < n_qtiles ? n_qtiles - 1 - rank : -1;
+  };
+  auto next_round = [&](int r) {
+    for (++r;; ++r) {
+      const int qt = qt_of(r);
+      if (qt < 0) return -1;
+      if (qt * BMPOS < n) return r;
+    }
+  };
+  int r = next_round(-1);
+  if (r < 0) return;  // the whole workgroup: no live q-tile (before any barrier)
 
   // K and V of (b, kvh) as raw buffers; token t's row starts at byte t * row_stride
-  // (PAGED: one buffer per (page, kv head) block, built per load).
+  // (PAGED: one buffer per (page, kv head) block, built per load). Q rows of head h:
+  // row i at byte i * q_stride.
   const uint32_t row_stride = (uint32_t)Hkv * ROWB;
   const size_t bkv_off = (size_t)b * S * Hkv * D + (size_t)kvh * D;
   const uint32_t extent = (uint32_t)(S - 1) * row_stride + ROWB;
   const u32x4_t k_rsrc = make_rsrc(k + bkv_off, extent);
   const u32x4_t v_rsrc = make_rsrc(v + bkv_off, extent);
+  const uint32_t q_stride = (uint32_t)Hq * ROWB;
 
-  // Q^T operand: lane holds dims 16s + 8*half .. +7 of query my_q, for s = 0..7. The
-  // softmax below takes the row max of the raw scores and applies the scale inside the
+  // The softmax below takes the row max of the raw scores and applies the scale inside the
   // exponent, which needs scale > 0: a negative scale is moved onto Q (sign flip, exact),
   // and a zero scale is raised to 1e-30 so that masked (-inf) scores still give exp2 = 0
   // (every finite score then maps to exp2(~0) = 1 in fp32, the uniform weights of scale 0).
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const float sl2 = fmaxf(fabsf(scale_log2), 1e-30f);
-  u32x4_t qop[8];
-  {
-    const bool ok = my_q < n;
-    const bf16_t* qrow = q + (((size_t)b * S + (ok ? my_q : 0)) * Hq + h) * D;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4_t t = *(const u32x4_t*)(qrow + 16 * s + 8 * half);
-      qop[s] = ok ? (t ^ qsign) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
 
+  // Item state (set per q-tile): first position q0, this wave's first row qa (a lane's
+  // query row is qa + lane % 32), the key tiles of the wave / workgroup and the first tile
+  // that needs the causal mask for this wave. Per-lane values are derived from fresh_lane()
+  // where they are used.
+  int q0 = 0, qa = 0, wave_tiles = 0, wg_tiles = 0, mask_from = 0;
+  // The next item's Q rows are requested at even phase 2 * u_pf (with V(u_pf)), into this
+  // wave's own LDS rows, which it read at phase 0.
+  bool has_next = false;
+  int u_pf = 1, qa_next = 0;
+
+  u32x4_t qop[8];
   f32x16_t oacc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
   float m_run = -INFINITY;
   float l_half = 0.f;
 
@@ -152,15 +195,25 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // +3 of K (ii = 0, 1) or V (ii = 2, 3), 16 lanes per row. A lane's byte offset in the
   // buffer is fixed up to the tile base; rows past S - 1 are clamped onto row S - 1.
   static_assert(WAVES * 2 == 16, "two loads move a K tile, two a V tile");
-  const uint32_t smem0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&smem[0][0][0];
-  uint32_t dma_off[4], dma_last[4];
+  const uint32_t smem0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&smem[0];
+  // (Computed per tile from a lane index the compiler cannot see through: offsets kept in
+  // registers for the whole kernel get spilled, and reloading a spilled value waits for every
+  // load in flight, the tile DMA included.)
+  struct DmaLane {
+    uint32_t off[4], last[4];
+  };
+  auto dma_lane = [&]() {
+    const int ln = fresh_lane();
+    DmaLane d;
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int r = 4 * ((ii & 1) * WAVES + w) + (lane >> 4);
-    const int chunk = (lane & 15) ^ (ii >= 2 ? v_swz(r) : k_swz(r));
-    dma_off[ii] = (uint32_t)r * row_stride + chunk * 16;
-    dma_last[ii] = (uint32_t)(S - 1) * row_stride + chunk * 16;
-  }
+    for (int ii = 0; ii < 4; ++ii) {
+      const int row = 4 * ((ii & 1) * WAVES + w) + (ln >> 4);
+      const int chunk = (ln & 15) ^ (ii >= 2 ? v_swz(row) : k_swz(row));
+      d.off[ii] = (uint32_t)row * row_stride + chunk * 16;
+      d.last[ii] = (uint32_t)(S - 1) * row_stride + chunk * 16;
+    }
+    return d;
+  };
   const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(smem0 + w * 1024);
   // PAGED: a load moves 4 consecutive keys, which share one 16-key page. Its first key
   // g0 (clamped onto end - 1) picks the page through the page table; a lane's key is
@@ -168,65 +221,116 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // masked, but their V must be finite), and its byte offset in the (page, kv head) block
   // is slot * 256 + the swizzled chunk.
   auto paged_dma = [&](const bf16_t* cache, int t, int ii, uint32_t lds) {
+    const int ln = fresh_lane();
     const int wi2 = (ii & 1) * WAVES + w;
     const int g0 = t * BN + 4 * wi2;
     const int gk = min(g0, end - 1);
     const int page = page_table[(size_t)b * max_pages + (gk >> 4)];
-    const int key = min(g0 + (lane >> 4), end - 1);
-    const int chunk = (lane & 15) ^ (ii >= 2 ? v_swz(4 * wi2 + (lane >> 4)) : k_swz(4 * wi2 + (lane >> 4)));
+    const int key = min(g0 + (ln >> 4), end - 1);
+    const int chunk = (ln & 15) ^ (ii >= 2 ? v_swz(4 * wi2 + (ln >> 4)) : k_swz(4 * wi2 + (ln >> 4)));
     const u32x4_t rsrc = make_rsrc(cache + ((size_t)page * Hkv + kvh) * 16 * D, 16 * ROWB);
     buffer_dma16(rsrc, (uint32_t)((key & 15) * ROWB + chunk * 16), lds);
   };
-  auto issue_k = [&](int t, int st) {  // K tile t into stage st
+  // (The LDS base goes through an empty asm statement so that the compiler adds the stage
+  // offsets per call instead of keeping every stage's address in its own scalar register.)
+  auto issue_k = [&](int t, int st, const DmaLane& d) {  // K tile t into stage st
     const uint32_t off = (uint32_t)t * BN * row_stride;
+    uint32_t lds = dma_lds;
+    asm volatile("" : "+s"(lds));
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       if constexpr (PAGED)
-        paged_dma(k_cache, t, ii, dma_lds + st * 2 * TILE + ii * WAVES * 1024);
+        paged_dma(k_cache, t, ii, lds + st * 2 * TILE + ii * WAVES * 1024);
       else
-        buffer_dma16(k_rsrc, min(dma_off[ii] + off, dma_last[ii]),
-                     dma_lds + st * 2 * TILE + ii * WAVES * 1024);
+        buffer_dma16(k_rsrc, min(d.off[ii] + off, d.last[ii]), lds + st * 2 * TILE + ii * WAVES * 1024);
     }
   };
-  auto issue_v = [&](int t, int st) {  // V tile t into stage st
+  auto issue_v = [&](int t, int st, const DmaLane& d) {  // V tile t into stage st
     const uint32_t off = (uint32_t)t * BN * row_stride;
+    uint32_t lds = dma_lds;
+    asm volatile("" : "+s"(lds));
 #pragma unroll
     for (int ii = 2; ii < 4; ++ii) {
       if constexpr (PAGED)
-        paged_dma(v_cache, t, ii, dma_lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
+        paged_dma(v_cache, t, ii, lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
       else
-        buffer_dma16(v_rsrc, min(dma_off[ii] + off, dma_last[ii]),
-                     dma_lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
+        buffer_dma16(v_rsrc, min(d.off[ii] + off, d.last[ii]),
+                     lds + st * 2 * TILE + TILE + (ii & 1) * WAVES * 1024);
     }
   };
 
-  // Per-lane LDS byte offsets, fixed for the whole kernel (stage, key block and row step
-  // are compile-time and become instruction offsets):
+  // Q rows qa .. qa + 31 of an item into this wave's 8 KiB of LDS, 4 rows (16 lanes each) per
+  // load: row i of the wave goes to LDS row i, its 16-byte chunks XOR-swizzled by i % 16 like
+  // the K rows. Rows past S - 1 are clamped onto row S - 1 (their queries are not live).
+  const uint32_t qbuf = __builtin_amdgcn_readfirstlane(smem0 + Q_OFF + w * 32 * ROWB);
+  // (The lane index is passed through an empty asm statement so that the compiler computes
+  // the offsets per call instead of keeping them live through the kernel.)
+  auto fetch_q = [&](int qa_item) {
+    const int ln = fresh_lane();
+    uint32_t lds = qbuf;
+    asm volatile("" : "+s"(lds));
+    const u32x4_t rsrc = make_rsrc(q + ((size_t)b * S * Hq + h) * D, (uint32_t)(S - 1) * q_stride + ROWB);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ri = 4 * j + (ln >> 4);
+      const int row = min(qa_item + ri, S - 1);
+      buffer_dma16(rsrc, (uint32_t)row * q_stride + (((ln & 15) ^ (ri & 15)) << 4),
+                   lds + j * 1024);
+    }
+  };
+
+  // Causal prefill: page ids of the current item's positions, entries (q0 / 16) + lane of
+  // the page-table row (clamped to the row), into this wave's 256 bytes of LDS.
+  auto fetch_pages = [&]() {
+    const int ln = fresh_lane();
+    uint32_t lds = __builtin_amdgcn_readfirstlane(smem0 + PT_OFF + w * 256);
+    asm volatile("" : "+s"(lds));
+    const u32x4_t rsrc = make_rsrc(page_table + (size_t)b * max_pages, (uint32_t)max_pages * 4);
+    buffer_dma4(rsrc, (uint32_t)min((q0 >> 4) + ln, max_pages - 1) * 4, lds);
+  };
+
+  // Per-lane LDS byte offsets (stage, key block and row step are compile-time and become
+  // instruction offsets):
   //   K, A operand of step s: row l32, 16-byte chunk (2s + half) ^ (l32 % 16);
   //   V^T, transpose reads: lane (g16, i16) reads row 4*(g16/2) + i16/4 (+16 sp + 8 r) at
   //   chunk 4*mbd + 2*(g16%2) + (i16%4)/2 with the row swizzle 4*(row % 4), i.e.
   //   4*(mbd ^ (i16/4)) + ..., byte (i16%2)*8 of the chunk.
-  uint32_t koff[8];
+  // These and the DMA offsets are recomputed at the start of every item from a lane index
+  // the compiler cannot see through: values kept live around the item loop would not fit
+  // in the register file next to the tile loop's.
+  uint32_t koff[8], voff[4];
+  auto set_lane_offsets = [&]() {
+    const int ln = fresh_lane();
+    const int l32x = ln & 31, hx = ln >> 5;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) koff[s] = smem0 + l32 * ROWB + (((2 * s + half) ^ (l32 & 15)) << 4);
-  const int g16 = lane >> 4;
-  const int i16 = lane & 15;
-  const uint32_t vlane = smem0 + TILE + (4 * (g16 >> 1) + (i16 >> 2)) * ROWB +
-                         (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 + (i16 & 1) * 8;
-  uint32_t voff[4];
+    for (int s = 0; s < 8; ++s) koff[s] = smem0 + l32x * ROWB + (((2 * s + hx) ^ (l32x & 15)) << 4);
+    const int g16 = ln >> 4;
+    const int i16 = ln & 15;
+    const uint32_t vlane = smem0 + TILE + (4 * (g16 >> 1) + (i16 >> 2)) * ROWB +
+                           (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 + (i16 & 1) * 8;
 #pragma unroll
-  for (int mbd = 0; mbd < 4; ++mbd) voff[mbd] = vlane + ((mbd ^ (i16 >> 2)) << 6);
+    for (int mbd = 0; mbd < 4; ++mbd) voff[mbd] = vlane + ((mbd ^ (i16 >> 2)) << 6);
+  };
 
   // S^T = K Q^T for the tile in stage ST: two 32-key blocks (16 MFMAs, two chains). The
   // K operands are read PF steps ahead so that LDS latency stays off the MFMA chain
   // (sched_barrier keeps the compiler from sinking the reads next to their use).
   f32x16_t sacc[2];
+  // K(0)'s buffer lies beyond the 16-bit offset field of the LDS reads: its base is added per
+  // read from a register the compiler may not hoist (keeping 8 more addresses live through
+  // the whole kernel would spill).
   auto scores = [&](auto st_tag) {
-    constexpr uint32_t SOFF = decltype(st_tag)::value * 2 * TILE;
+    constexpr int ST = decltype(st_tag)::value;
+    constexpr uint32_t SOFF = ST == 2 ? 0 : ST * 2 * TILE;
+    uint32_t base = 0;
+    if constexpr (ST == 2) {
+      base = K0_OFF;
+      asm volatile("" : "+v"(base));
+    }
     constexpr int PF = 3;
     auto kread = [&](int s, int mb) {
       return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
-          koff[s] + SOFF + mb * 32 * ROWB);
+          koff[s] + base + SOFF + mb * 32 * ROWB);
     };
     u32x4_t ka[PF + 1][2];
 #pragma unroll
@@ -257,7 +361,8 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   u32x4_t pop[4];
   auto softmax = [&](int kt, bool diag) {
     if (diag) {
-      const int lim = my_pos - kt * BN - 4 * half;
+      const int ln = fresh_lane();
+      const int lim = p + qa + (ln & 31) - kt * BN - 4 * (ln >> 5);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -331,29 +436,52 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // each group on every SIMD. Time is cut into phases by workgroup barriers; in each phase
   // one group runs its MFMA phase (PV of tile t, then the scores of tile t+1) while the
   // other runs its softmax phase (VALU), so matrix and vector units of a SIMD work at the
-  // same time. Global phase p: group A runs softmax(t) at p = 2t+1 and MFMA(t) at
-  // p = 2t+2 (scores(0) at p = 0); group B runs one phase later. Hence K(t) is read in
-  // phases 2t, 2t+1 and V(t) in phases 2t+2, 2t+3. Tile t lives in stage t % 2; at every
-  // even phase 2u all waves issue the DMA of K(u+1) and V(u), whose stages were last read
-  // in phase 2u-1, and wait for it (vmcnt) before the barrier that opens phase 2u+2.
-  // Every wave passes 2 * wg_tiles + 2 barriers.
+  // same time. Global phase p of an item: group A runs softmax(t) at p = 2t+1 and MFMA(t)
+  // at p = 2t+2 (scores(0) at p = 0); group B runs one phase later. Hence K(t) is read in
+  // phases 2t, 2t+1 and V(t) in phases 2t+2, 2t+3. Tile t >= 1 lives in stage t % 2 (K(0)
+  // in its own buffer); at every even phase 2u all waves issue the DMA of K(u+1) and V(u),
+  // whose stages were last read in phase 2u-1, and wait for it (vmcnt) before the barrier
+  // that opens phase 2u+2. At phase 2 * u_pf the waves also request the next item's Q rows
+  // (8 loads per wave, issued after V(u_pf)), so the wait before phase 2 * u_pf + 2 leaves
+  // those 8 in flight: loads complete in issue order. Every wave passes 2 * wg_tiles + 2
+  // barriers per item.
   auto bar = [&]() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();
   };
   auto even_phase_dma = [&](int u, auto par_tag) {  // u % 2 == par
     constexpr int PAR = decltype(par_tag)::value;
-    if (u + 1 < wg_tiles) issue_k(u + 1, PAR ^ 1);
-    if (u < wg_tiles) issue_v(u, PAR);
+    DmaLane d{};
+    if constexpr (!PAGED) d = dma_lane();
+    if (u + 1 < wg_tiles) issue_k(u + 1, PAR ^ 1, d);
+    if (u < wg_tiles) issue_v(u, PAR, d);
+    if (u == u_pf) {
+      if (has_next) fetch_q(qa_next);
+      if constexpr (!PAGED) fetch_pages();
+    }
+  };
+  // Before the barrier that opens phase 2t+2: the tile loads of phase 2t must have landed;
+  // at t == u_pf the loads issued after them (the next item's Q rows, the page ids) may not.
+  auto wait_dma = [&](int t) {
+    if (t == u_pf) {
+      if (has_next) {
+        if constexpr (PAGED) wait_vmcnt<8>(); else wait_vmcnt<9>();
+      } else {
+        if constexpr (PAGED) wait_vmcnt<0>(); else wait_vmcnt<1>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  using PK0 = std::integral_constant<int, 2>;  // K(0)'s own buffer
   // tile t (parity PAR) for a wave of group A: softmax at phase 2t+1, MFMA at 2t+2
   auto tile_a = [&](int t, auto par_tag) {
     constexpr int PAR = decltype(par_tag)::value;
     bar();  // phase 2t+1
     if (t < wave_tiles) softmax(t, t >= mask_from);
-    wait_vmcnt<0>();
+    wait_dma(t);
     bar();  // phase 2t+2
     even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
     if (t < wave_tiles) pv(par_tag);
@@ -362,7 +490,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // tile t for a wave of group B: softmax at phase 2t+2, MFMA at 2t+3
   auto tile_b = [&](int t, auto par_tag) {
     constexpr int PAR = decltype(par_tag)::value;
-    wait_vmcnt<0>();
+    wait_dma(t);
     bar();  // phase 2t+2
     even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
     if (t < wave_tiles) softmax(t, t >= mask_from);
@@ -371,60 +499,211 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     if (t + 1 < wave_tiles) scores(std::integral_constant<int, PAR ^ 1>{});
   };
 
-  issue_k(0, 0);
-  if constexpr (!PAGED) {
-  // KV append: this workgroup copies the new K/V rows of its own positions
-  // [q0, q0 + BMPOS) of KV head kvh into their cache slots (slot pos % 16 of page
-  // page_table[b][pos / 16]); every position of every (b, kvh) is owned by exactly one
-  // workgroup. The rows were just requested by the first tile's DMA, so they come from L2.
-  {
+  // KV append (causal prefill only): a workgroup copies the new K/V rows of the positions
+  // [q0i, q0i + BMPOS) of an item it finished, for KV head kvh, into their cache slots (slot
+  // pos % 16 of page page_table[b][pos / 16]); every position of every (b, kvh) belongs to
+  // exactly one item. The rows were streamed as the item's last K/V tiles, so the reads
+  // mostly hit L2. Eight 16-byte chunks per thread are loaded before any is stored.
+  auto append_rows = [&](int q0i, int tid, int nthreads) {
+    asm volatile("" : "+v"(tid));
+    const int nrows = min(BMPOS, S - q0i);
+    const int total = nrows * 32;  // 16-byte chunks: K then V, 16 per row
+    for (int base = 0; base < total; base += 8 * nthreads) {
+      u32x4_t x[8];
+      bf16_t* dst[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = min(base + u * nthreads + tid, total - 1);
+        const int is_v = idx >= nrows * 16;
+        const int rem = idx - is_v * nrows * 16;
+        const int pos = q0i + (rem >> 4), c = rem & 15;
+        const int page = page_table[(size_t)b * max_pages + (pos >> 4)];
+        x[u] = *(const u32x4_t*)((is_v ? v : k) + ((size_t)(b * S + pos) * Hkv + kvh) * D + c * 8);
+        dst[u] = (is_v ? v_cache : k_cache) + (((size_t)page * Hkv + kvh) * 16 + (pos & 15)) * D + c * 8;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (base + u * nthreads + tid < total) *(u32x4_t*)dst[u] = x[u];
+    }
+  };
+  // With G >= 2 an item's positions lie in its last one or two key tiles, which are still in
+  // LDS when group A has finished the item (K(T-1), V(T-1) in stage (T-1) % 2, K(T-2) and
+  // V(T-2) in the other stage or, for tile 0, K(0)'s buffer; nothing is loaded over them
+  // before the next item starts), and the page ids were fetched into LDS: the append is LDS
+  // reads and global stores only.
+  auto append_from_lds = [&]() {
+    const int tid = fresh_lane() + kWave * w;  // group A: 256 threads
     const int nrows = min(BMPOS, S - q0);
-    for (int idx = (int)threadIdx.x; idx < nrows * 32; idx += THREADS) {
-      const int is_v = idx >= nrows * 16;
-      const int rem = idx - is_v * nrows * 16;
-      const int pos = q0 + (rem >> 4), c = rem & 15;
-      const int page = page_table[(size_t)b * max_pages + (pos >> 4)];
-      const u32x4_t x =
-          *(const u32x4_t*)((is_v ? v : k) + ((size_t)(b * S + pos) * Hkv + kvh) * D + c * 8);
-      *(u32x4_t*)((is_v ? v_cache : k_cache) + (((size_t)page * Hkv + kvh) * 16 + (pos & 15)) * D +
-                  c * 8) = x;
+    const int total = nrows * 32;  // 16-byte chunks: K then V, 16 per row
+    for (int base = 0; base < total; base += 8 * 4 * kWave) {
+      u32x4_t x[8];
+      bf16_t* dst[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = min(base + u * 4 * kWave + tid, total - 1);
+        const int is_v = idx >= nrows * 16;
+        const int rem = idx - is_v * nrows * 16;
+        const int pos = q0 + (rem >> 4), c = rem & 15;
+        const int t = pos / BN, row = pos % BN;
+        const uint32_t tile = is_v ? (uint32_t)(t & 1) * 2 * TILE + TILE
+                                   : (t == 0 ? K0_OFF : (uint32_t)(t & 1) * 2 * TILE);
+        const int swz = is_v ? v_swz(row) : k_swz(row);
+        x[u] = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
+            smem0 + tile + row * ROWB + ((c ^ swz) << 4));
+        const int page = *(const __attribute__((address_space(3))) int*)(uintptr_t)(
+            smem0 + PT_OFF + w * 256 + ((pos >> 4) - (q0 >> 4)) * 4);
+        dst[u] = (is_v ? v_cache : k_cache) + (((size_t)page * Hkv + kvh) * 16 + (pos & 15)) * D + c * 8;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (base + u * 4 * kWave + tid < total) *(u32x4_t*)dst[u] = x[u];
     }
-  }
-  }
-  wait_vmcnt<0>();  // K(0) has landed (and the append's stores have completed)
-  bar();  // phase 0
-  even_phase_dma(0, P0{});
-  if (w < 4) {
-    if (wave_tiles > 0) scores(P0{});
-    for (int t = 0; t < wg_tiles; t += 2) {
-      tile_a(t, P0{});
-      if (t + 1 < wg_tiles) tile_a(t + 1, P1{});
-    }
-    bar();
-  } else {
-    bar();  // phase 1
-    if (wave_tiles > 0) scores(P0{});
-    for (int t = 0; t < wg_tiles; t += 2) {
-      tile_b(t, P0{});
-      if (t + 1 < wg_tiles) tile_b(t + 1, P1{});
-    }
-  }
-  wait_vmcnt<0>();
+  };
 
-  // ---- epilogue: O = O^T / l, bf16, 4 consecutive dims per store ----
-  if (wave_tiles == 0 || my_q >= n) return;
-  const float l_tot = l_half + __shfl_xor(l_half, 32);
-  const float inv = 1.0f / l_tot;
-  bf16_t* orow = out + (((size_t)b * S + my_q) * Hq + h) * D;
+  // Output of one wave's 32 rows (O = O^T / l, bf16). The MFMA layout gives a lane 4
+  // consecutive dims of one row, so the tile is first written to 8 KiB of LDS at sbase (16-byte
+  // chunks XOR-swizzled by row % 16) and read back as whole rows, 16 lanes per 256-byte row:
+  // each global store then writes four complete rows instead of 16 bytes of each of 32 rows.
+  auto store_output = [&](uint32_t sbase, int qa_e) {
+    const int ln = fresh_lane();
+    const int rw = ln & 31, hf = ln >> 5;
+    const float l_tot = l_half + __shfl_xor(l_half, 32);
+    const float inv = 1.0f / l_tot;  // not finite on rows that are not stored
 #pragma unroll
-  for (int mbd = 0; mbd < 4; ++mbd)
+    for (int mbd = 0; mbd < 4; ++mbd)
 #pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      const int dim = 32 * mbd + 8 * jq + 4 * half;
-      const u32x2_t pk = {pack_bf16x2(oacc[mbd][4 * jq + 0] * inv, oacc[mbd][4 * jq + 1] * inv),
-                          pack_bf16x2(oacc[mbd][4 * jq + 2] * inv, oacc[mbd][4 * jq + 3] * inv)};
-      *(u32x2_t*)(orow + dim) = pk;
+      for (int jq = 0; jq < 4; ++jq) {
+        const u32x2_t pk = {pack_bf16x2(oacc[mbd][4 * jq + 0] * inv, oacc[mbd][4 * jq + 1] * inv),
+                            pack_bf16x2(oacc[mbd][4 * jq + 2] * inv, oacc[mbd][4 * jq + 3] * inv)};
+        *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)(
+            sbase + rw * ROWB + (((4 * mbd + jq) ^ (rw & 15)) << 4) + 8 * hf) = pk;
+      }
+    // rows of head h as a raw buffer (row i at byte i * Hq * ROWB); rows past the live ones get
+    // an offset beyond the buffer and the hardware drops their stores
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        out + ((size_t)b * S * Hq + h) * D, 0, (int)((uint32_t)(S - 1) * q_stride + ROWB), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 4 * i + (ln >> 4), c = ln & 15;
+      const u32x4_t x = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
+          sbase + rr * ROWB + ((c ^ (rr & 15)) << 4));
+      const int row = qa_e + rr;
+      const uint32_t off = row < n ? (uint32_t)row * q_stride + c * 16 : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)off, 0, 0);
     }
+  };
+  // Direct form (each lane stores its 4-dim pieces), for group A with G = 2, whose free LDS
+  // stage still holds rows the KV append reads.
+  auto store_output_direct = [&](int qa_e) {
+    const int ln = fresh_lane();
+    const int my_q = qa_e + (ln & 31);
+    const float l_tot = l_half + __shfl_xor(l_half, 32);
+    if (my_q < n) {
+      const float inv = 1.0f / l_tot;
+      bf16_t* orow = out + (((size_t)b * S + my_q) * Hq + h) * D;
+#pragma unroll
+      for (int mbd = 0; mbd < 4; ++mbd)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const int dim = 32 * mbd + 8 * jq + 4 * (ln >> 5);
+          const u32x2_t pk = {pack_bf16x2(oacc[mbd][4 * jq + 0] * inv, oacc[mbd][4 * jq + 1] * inv),
+                              pack_bf16x2(oacc[mbd][4 * jq + 2] * inv, oacc[mbd][4 * jq + 3] * inv)};
+          *(u32x2_t*)(orow + dim) = pk;
+        }
+    }
+  };
+  // Group B stores an item's output at the start of the next item (phase 0, in which it has no
+  // other work), staged in its own Q rows of LDS once it has read them; group A stores at the
+  // end of the item, in phase 2T+1, staged in stage T % 2, which no wave reads any more then
+  // (the append reads tiles T-1 and, with G = 2, T-2).
+  int qa_prev = 0;
+  bool b_pending = false;
+
+  set_lane_offsets();
+  {
+    DmaLane d{};
+    if constexpr (!PAGED) d = dma_lane();
+    issue_k(0, 2, d);  // K(0) into its own buffer, once
+  }
+  fetch_q(qt_of(r) * BMPOS + 32 * (w % PB));
+  wait_vmcnt<0>();  // K(0) and the first item's Q rows have landed
+  for (;;) {
+    q0 = qt_of(r) * BMPOS;
+    qa = q0 + 32 * (w % PB);
+    wave_tiles = qa < n ? (p + min(qa + 31, n - 1)) / BN + 1 : 0;
+    wg_tiles = (p + min(q0 + BMPOS, n) - 1) / BN + 1;
+    mask_from = (p + qa) / BN;
+    const int rn = next_round(r);
+    has_next = rn >= 0;
+    u_pf = max(wg_tiles - 1, 1);
+    qa_next = has_next ? qt_of(rn) * BMPOS + 32 * (w % PB) : 0;
+
+    set_lane_offsets();
+    bar();  // phase 0; every wave is done with the previous item, its Q rows have landed
+    {
+      // Q^T operand: lane holds dims 16s + 8*half .. +7 of query my_q, for s = 0..7 (the
+      // row's swizzle is the K rows', so the per-lane offsets are koff's; the base is kept
+      // in a register the compiler may not hoist, as for K(0))
+      const bool ok = qa + (fresh_lane() & 31) < n;
+      uint32_t qb = qbuf - smem0;
+      asm volatile("" : "+v"(qb));
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const u32x4_t t =
+            *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(koff[s2] + qb);
+        qop[s2] = ok ? (t ^ qsign) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    if (w >= 4 && b_pending) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the Q rows are in registers
+      store_output(qbuf, qa_prev);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
+    m_run = -INFINITY;
+    l_half = 0.f;
+    even_phase_dma(0, P0{});
+    if (w < 4) {
+      if (wave_tiles > 0) scores(PK0{});
+      for (int t = 0; t < wg_tiles; t += 2) {
+        tile_a(t, P0{});
+        if (t + 1 < wg_tiles) tile_a(t + 1, P1{});
+      }
+      bar();
+    } else {
+      bar();  // phase 1
+      if (wave_tiles > 0) scores(PK0{});
+      for (int t = 0; t < wg_tiles; t += 2) {
+        tile_b(t, P0{});
+        if (t + 1 < wg_tiles) tile_b(t + 1, P1{});
+      }
+    }
+    // The next item's Q rows and this item's page ids have landed (requested three phases
+    // earlier); waiting here, before the stores below, keeps the stores' completion off the
+    // next item's start.
+    wait_vmcnt<0>();
+    if (w < 4) {
+      if constexpr (G == 2 && !PAGED)
+        store_output_direct(qa);
+      else
+        store_output(smem0 + (uint32_t)(wg_tiles & 1) * 2 * TILE + w * 32 * ROWB, qa);
+    } else {
+      qa_prev = qa;
+      b_pending = true;
+    }
+    if constexpr (!PAGED) {
+      if (w < 4) {
+        if constexpr (G == 1)
+          append_rows(q0, fresh_lane() + kWave * w, 4 * kWave);
+        else
+          append_from_lds();
+      }
+    }
+    if (!has_next) break;
+    r = rn;
+  }
+  if (w >= 4) store_output(qbuf, qa);  // no next item: the Q rows are free
+  wait_vmcnt<0>();
 }
 
 // Chunked prefill, step 1: new[b][i] (i < new_lens[b]) -> cache slot of position
@@ -452,6 +731,21 @@ __global__ __launch_bounds__(256) void append_at_kernel(
   *(u32x4_t*)(v_cache + dst) = *(const u32x4_t*)(v + src);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return 0;
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
 template <int G, bool PAGED>
 static int launch_g(const void* q, const void* k, const void* v, void* out, void* k_cache,
                     void* v_cache, const int32_t* page_table, const int32_t* past_lens,
@@ -459,11 +753,17 @@ static int launch_g(const void* q, const void* k, const void* v, void* out, void
                     float scale, hipStream_t s) {
   constexpr int BMPOS = 256 / G;
   const int n_qtiles = (S + BMPOS - 1) / BMPOS;
-  dim3 grid((unsigned)(B * Hkv), (unsigned)n_qtiles);
-  hipLaunchKernelGGL((prefill_causal_kernel<G, PAGED>), grid, dim3(prefill::THREADS), 0, s,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)out,
-                     (bf16_t*)k_cache, (bf16_t*)v_cache, page_table, past_lens, new_lens,
-                     max_pages, S, Hq, Hkv, scale * kLog2e, n_qtiles);
+  const int cus = device_cus();
+  if (cus <= 0) return GQA_ERR_LAUNCH;
+  // One resident workgroup per compute unit: nbkv pairs x rows_per_round workgroups each
+  // (at least one workgroup per pair; never more rows than q-tiles).
+  const int nbkv = B * Hkv;
+  const int rows = std::max(1, std::min(cus / nbkv, n_qtiles));
+  hipLaunchKernelGGL((prefill_causal_kernel<G, PAGED>), dim3((unsigned)(nbkv * rows)),
+                     dim3(prefill::THREADS), 0, s, (const bf16_t*)q, (const bf16_t*)k,
+                     (const bf16_t*)v, (bf16_t*)out, (bf16_t*)k_cache, (bf16_t*)v_cache,
+                     page_table, past_lens, new_lens, max_pages, S, Hq, Hkv, scale * kLog2e,
+                     n_qtiles, nbkv, rows);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
