@@ -432,6 +432,60 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     }
   };
 
+  // One MFMA phase with both halves: PV of tile t (V from stage PV_ST) and the scores of tile
+  // t+1 (K from stage SC_ST), their MFMAs interleaved one for one. The PV operands come from
+  // transpose reads, which the LDS serves at about half the rate of the score loop's b128
+  // reads; four waves running PV alone outrun the LDS, the mixed stream does not.
+  auto pv_scores = [&](auto pv_tag, auto sc_tag) {
+    constexpr uint32_t VOFF = decltype(pv_tag)::value * 2 * TILE;
+    constexpr uint32_t KOFF = decltype(sc_tag)::value * 2 * TILE;
+    constexpr int PF = 2;
+    auto vread = [&](int i) {  // operand of PV MFMA i = 4 sp + mbd
+      const int sp = i >> 2, mbd = i & 3;
+      const uint32_t a0p = voff[mbd] + VOFF + (16 * sp) * ROWB;
+      const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)a0p);
+      const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(a0p + 8 * ROWB));
+      const u32x2_t a0 = __builtin_bit_cast(u32x2_t, t0);
+      const u32x2_t a1 = __builtin_bit_cast(u32x2_t, t1);
+      return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    };
+    auto kread = [&](int i) {  // operand of score MFMA i = 2 s + mb
+      return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
+          koff[i >> 1] + KOFF + (i & 1) * 32 * ROWB);
+    };
+    u32x4_t va[PF + 1], ka[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      va[i] = vread(i);
+      ka[i] = kread(i);
+    }
+    sacc[0] = f32x16_t{};
+    sacc[1] = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + PF < 16) {
+        va[(i + PF) % (PF + 1)] = vread(i + PF);
+        ka[(i + PF) % (PF + 1)] = kread(i + PF);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, va[i % (PF + 1)]),
+          __builtin_bit_cast(bf16x8_t, pop[i >> 2]), oacc[i & 3], 0, 0, 0);
+      sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, ka[i % (PF + 1)]),
+          __builtin_bit_cast(bf16x8_t, qop[i >> 1]), sacc[i & 1], 0, 0, 0);
+    }
+  };
+  // PV(t) and scores(t+1) of this wave. On the wave's last tile the scores half runs too (on
+  // whatever stage (t+1) % 2 holds; softmax never reads them): one code path for the phase
+  // keeps the register allocation of the loop within the register file.
+  auto mfma_phase = [&](int t, auto par_tag) {
+    constexpr int PAR = decltype(par_tag)::value;
+    if (t < wave_tiles) pv_scores(par_tag, std::integral_constant<int, PAR ^ 1>{});
+  };
+
   // Two wave groups in antiphase. Waves 0-3 (group A) and 4-7 (group B) put one wave of
   // each group on every SIMD. Time is cut into phases by workgroup barriers; in each phase
   // one group runs its MFMA phase (PV of tile t, then the scores of tile t+1) while the
@@ -484,8 +538,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     wait_dma(t);
     bar();  // phase 2t+2
     even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
-    if (t < wave_tiles) pv(par_tag);
-    if (t + 1 < wave_tiles) scores(std::integral_constant<int, PAR ^ 1>{});
+    mfma_phase(t, par_tag);
   };
   // tile t for a wave of group B: softmax at phase 2t+2, MFMA at 2t+3
   auto tile_b = [&](int t, auto par_tag) {
@@ -495,8 +548,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
     if (t < wave_tiles) softmax(t, t >= mask_from);
     bar();  // phase 2t+3
-    if (t < wave_tiles) pv(par_tag);
-    if (t + 1 < wave_tiles) scores(std::integral_constant<int, PAR ^ 1>{});
+    mfma_phase(t, par_tag);
   };
 
   // KV append (causal prefill only): a workgroup copies the new K/V rows of the positions
