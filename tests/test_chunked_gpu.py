@@ -123,3 +123,14 @@ def test_chunked_prefill_deterministic(gpu_lib):
                               x.new_lens, scale=x.scale, out=torch.zeros_like(x.q))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_chunked_prefill_items_without_live_rows(gpu_lib):
+    """Chunks much shorter than the padded length S: the heaviest q-tiles of a sequence hold
+    no live row and are skipped, workgroups of a sequence with an empty chunk do nothing,
+    and the others walk several q-tiles; sampled heads against the oracle."""
+    print("[chunked] dead items", flush=True)
+    x = synth.chunked_inputs(4, 1024, 32, 8, 128, P, [0, 300, 2000, 50], [1024, 500, 64, 0],
+                             seed=1717, device=DEV)
+    rows = [(0, 3), (0, 30), (1, 9), (1, 17), (2, 0), (2, 31)]
+    _run_and_check(gpu_lib, x, "chunked dead items", rows=rows)

@@ -126,3 +126,37 @@ def test_prefill_scale_sign_and_magnitude(gpu_lib, scale):
     c = x.to("cpu")
     ref = oracle.prefill_causal(c.q, c.k, c.v, scale)
     assert_close(out, ref, "bf16", f"prefill scale={scale}")
+
+
+def test_prefill_more_kv_pairs_than_compute_units(gpu_lib):
+    """B * Hkv = 264 (b, kv head) pairs: more than one workgroup per compute unit, so each
+    workgroup walks every q-tile of its pair; full output and append against the oracle."""
+    print("[prefill] 264 pairs", flush=True)
+    x = synth.prefill_inputs(66, 96, 16, 4, 128, 16, seed=264, device=DEV)
+    kb, vb = x.k_cache.cpu(), x.v_cache.cpu()
+    out = _run(gpu_lib, x)
+    c = x.to("cpu")
+    ref = oracle.prefill_causal(c.q, c.k, c.v, c.scale)
+    assert_close(out, ref, "bf16", "prefill 264 pairs")
+    _check_append(x, kb, vb)
+
+
+@pytest.mark.parametrize("B,S,hq,hkv", [(8, 640, 64, 8), (16, 1100, 8, 2), (16, 600, 16, 8),
+                                         (32, 700, 4, 4)])
+def test_prefill_several_q_tiles_per_workgroup(gpu_lib, B, S, hq, hkv):
+    """More q-tiles than workgroups per (b, kv head) pair on a 256-CU device: every
+    workgroup processes several q-tiles in a row (G = 8, 4, 2, 1; the last round only partly
+    filled, S not a multiple of the q-tile); sampled heads against the oracle, the whole
+    append bit for bit."""
+    print(f"[prefill] several items B={B} S={S} {hq}x{hkv}", flush=True)
+    x = synth.prefill_inputs(B, S, hq, hkv, 128, 16, seed=B * S + hq, device=DEV)
+    kb, vb = x.k_cache.cpu(), x.v_cache.cpu()
+    out = _run(gpu_lib, x)
+    _check_append(x, kb, vb)
+    c = x.to("cpu")
+    rows = [(0, 0), (B - 1, hq - 1), (B // 2, hq // 2 + 1)]
+    ref = oracle.prefill_causal_rows(c.q, c.k, c.v, c.scale, rows)
+    got = np.stack([to_f64(out[b, :, h]) for (b, h) in rows])
+    want = np.stack([ref[r] for r in rows])
+    assert_close(got, want, "bf16", f"prefill several items B={B} S={S}")
+    assert torch.isfinite(out.float()).all()
