@@ -319,7 +319,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // K(0)'s buffer lies beyond the 16-bit offset field of the LDS reads: its base is added per
   // read from a register the compiler may not hoist (keeping 8 more addresses live through
   // the whole kernel would spill).
-  auto scores = [&](auto st_tag) {
+  auto scores = [&](auto st_tag, auto&& hook) {
     constexpr int ST = decltype(st_tag)::value;
     constexpr uint32_t SOFF = ST == 2 ? 0 : ST * 2 * TILE;
     uint32_t base = 0;
@@ -352,6 +352,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
         sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, ka[s % (PF + 1)][mb]),
             __builtin_bit_cast(bf16x8_t, qop[s]), sacc[mb], 0, 0, 0);
+      hook(s);
     }
   };
 
@@ -616,6 +617,21 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // consecutive dims of one row, so the tile is first written to 8 KiB of LDS at sbase (16-byte
   // chunks XOR-swizzled by row % 16) and read back as whole rows, 16 lanes per 256-byte row:
   // each global store then writes four complete rows instead of 16 bytes of each of 32 rows.
+  // rows 4i .. 4i+3 of a staged output tile to the output (rows of head h as a raw buffer, row
+  // i at byte i * Hq * ROWB; rows past the live ones get an offset beyond the buffer and the
+  // hardware drops their stores)
+  auto store_rows = [&](uint32_t sbase, int qa_e, int i) {
+    const int ln = fresh_lane();
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        out + ((size_t)b * S * Hq + h) * D, 0, (int)((uint32_t)(S - 1) * q_stride + ROWB), 0x00020000);
+    const int rr = 4 * i + (ln >> 4), c = ln & 15;
+    const u32x4_t x = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
+        sbase + rr * ROWB + ((c ^ (rr & 15)) << 4));
+    const int row = qa_e + rr;
+    const uint32_t off = row < n ? (uint32_t)row * q_stride + c * 16 : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)off, 0, 0);
+  };
+  // Stage this wave's output tile in LDS at sbase and, unless qa_e < 0, store it.
   auto store_output = [&](uint32_t sbase, int qa_e) {
     const int ln = fresh_lane();
     const int rw = ln & 31, hf = ln >> 5;
@@ -630,18 +646,9 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
         *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)(
             sbase + rw * ROWB + (((4 * mbd + jq) ^ (rw & 15)) << 4) + 8 * hf) = pk;
       }
-    // rows of head h as a raw buffer (row i at byte i * Hq * ROWB); rows past the live ones get
-    // an offset beyond the buffer and the hardware drops their stores
-    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-        out + ((size_t)b * S * Hq + h) * D, 0, (int)((uint32_t)(S - 1) * q_stride + ROWB), 0x00020000);
+    if (qa_e >= 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = 4 * i + (ln >> 4), c = ln & 15;
-      const u32x4_t x = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
-          sbase + rr * ROWB + ((c ^ (rr & 15)) << 4));
-      const int row = qa_e + rr;
-      const uint32_t off = row < n ? (uint32_t)row * q_stride + c * 16 : 0x80000000u;
-      __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)off, 0, 0);
+      for (int i = 0; i < 8; ++i) store_rows(sbase, qa_e, i);
     }
   };
   // Direct form (each lane stores its 4-dim pieces), for group A with G = 2, whose free LDS
@@ -664,10 +671,10 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
         }
     }
   };
-  // Group B stores an item's output at the start of the next item (phase 0, in which it has no
-  // other work), staged in its own Q rows of LDS once it has read them; group A stores at the
-  // end of the item, in phase 2T+1, staged in stage T % 2, which no wave reads any more then
-  // (the append reads tiles T-1 and, with G = 2, T-2).
+  // Group B stages an item's output at the start of the next item (phase 0, in which it has no
+  // other work) in its own Q rows of LDS once it has read them, and stores it between the
+  // MFMAs of its phase 1; group A stores at the end of the item, in phase 2T+1, staged in stage
+  // T % 2, which no wave reads any more then (the append reads tiles T-1 and, with G = 2, T-2).
   int qa_prev = 0;
   bool b_pending = false;
 
@@ -708,7 +715,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     }
     if (w >= 4 && b_pending) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the Q rows are in registers
-      store_output(qbuf, qa_prev);
+      store_output(qbuf, -1);  // staged only: stored between the MFMAs of phase 1
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
@@ -716,7 +723,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     l_half = 0.f;
     even_phase_dma(0, P0{});
     if (w < 4) {
-      if (wave_tiles > 0) scores(PK0{});
+      if (wave_tiles > 0) scores(PK0{}, [](int) {});
       for (int t = 0; t < wg_tiles; t += 2) {
         tile_a(t, P0{});
         if (t + 1 < wg_tiles) tile_a(t + 1, P1{});
@@ -724,7 +731,13 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
       bar();
     } else {
       bar();  // phase 1
-      if (wave_tiles > 0) scores(PK0{});
+      if (wave_tiles > 0) {
+        scores(PK0{}, [&](int i) {
+          if (b_pending) store_rows(qbuf, qa_prev, i);
+        });
+      } else if (b_pending) {
+        for (int i = 0; i < 8; ++i) store_rows(qbuf, qa_prev, i);
+      }
       for (int t = 0; t < wg_tiles; t += 2) {
         tile_b(t, P0{});
         if (t + 1 < wg_tiles) tile_b(t + 1, P1{});
