@@ -105,7 +105,7 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t num_reco
 // one pair run on the XCD of its workgroups (workgroup g runs on XCD g % 8, and c % 8 ==
 // g % 8 when 8 divides nbkv) and share its L2. Between two items the workgroup does not
 // drain: the next item's Q rows are fetched into LDS while the current item still runs,
-// and its output is stored after the next item has started.
+// and half of an item's output (group B's) is stored after the next item has started.
 template <int G, bool PAGED>
 __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_causal_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -295,9 +295,9 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   //   V^T, transpose reads: lane (g16, i16) reads row 4*(g16/2) + i16/4 (+16 sp + 8 r) at
   //   chunk 4*mbd + 2*(g16%2) + (i16%4)/2 with the row swizzle 4*(row % 4), i.e.
   //   4*(mbd ^ (i16/4)) + ..., byte (i16%2)*8 of the chunk.
-  // These and the DMA offsets are recomputed at the start of every item from a lane index
-  // the compiler cannot see through: values kept live around the item loop would not fit
-  // in the register file next to the tile loop's.
+  // These are recomputed at the start of every item (the DMA offsets for every tile) from a
+  // lane index the compiler cannot see through: values kept live around the item loop would
+  // not fit in the register file next to the tile loop's.
   uint32_t koff[8], voff[4];
   auto set_lane_offsets = [&]() {
     const int ln = fresh_lane();
@@ -433,8 +433,8 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     }
   };
 
-  // One MFMA phase with both halves: PV of tile t (V from stage PV_ST) and the scores of tile
-  // t+1 (K from stage SC_ST), their MFMAs interleaved one for one. The PV operands come from
+  // One MFMA phase with both halves: PV of tile t (V from the stage of pv_tag) and the scores
+  // of tile t+1 (K from the stage of sc_tag), their MFMAs interleaved one for one. The PV operands come from
   // transpose reads, which the LDS serves at about half the rate of the score loop's b128
   // reads; four waves running PV alone outrun the LDS, the mixed stream does not.
   auto pv_scores = [&](auto pv_tag, auto sc_tag) {
@@ -489,17 +489,17 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
 
   // Two wave groups in antiphase. Waves 0-3 (group A) and 4-7 (group B) put one wave of
   // each group on every SIMD. Time is cut into phases by workgroup barriers; in each phase
-  // one group runs its MFMA phase (PV of tile t, then the scores of tile t+1) while the
-  // other runs its softmax phase (VALU), so matrix and vector units of a SIMD work at the
-  // same time. Global phase p of an item: group A runs softmax(t) at p = 2t+1 and MFMA(t)
+  // one group runs its MFMA phase (PV of tile t interleaved with the scores of tile t+1)
+  // while the other runs its softmax phase (VALU), so matrix and vector units of a SIMD work
+  // at the same time. Global phase p of an item: group A runs softmax(t) at p = 2t+1 and MFMA(t)
   // at p = 2t+2 (scores(0) at p = 0); group B runs one phase later. Hence K(t) is read in
   // phases 2t, 2t+1 and V(t) in phases 2t+2, 2t+3. Tile t >= 1 lives in stage t % 2 (K(0)
   // in its own buffer); at every even phase 2u all waves issue the DMA of K(u+1) and V(u),
   // whose stages were last read in phase 2u-1, and wait for it (vmcnt) before the barrier
   // that opens phase 2u+2. At phase 2 * u_pf the waves also request the next item's Q rows
-  // (8 loads per wave, issued after V(u_pf)), so the wait before phase 2 * u_pf + 2 leaves
-  // those 8 in flight: loads complete in issue order. Every wave passes 2 * wg_tiles + 2
-  // barriers per item.
+  // (8 loads per wave) and, for the causal prefill, the item's page ids (1 load), issued
+  // after V(u_pf), so the wait before phase 2 * u_pf + 2 leaves those in flight: loads
+  // complete in issue order. Every wave passes 2 * wg_tiles + 2 barriers per item.
   auto bar = [&]() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();
@@ -555,8 +555,9 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // KV append (causal prefill only): a workgroup copies the new K/V rows of the positions
   // [q0i, q0i + BMPOS) of an item it finished, for KV head kvh, into their cache slots (slot
   // pos % 16 of page page_table[b][pos / 16]); every position of every (b, kvh) belongs to
-  // exactly one item. The rows were streamed as the item's last K/V tiles, so the reads
-  // mostly hit L2. Eight 16-byte chunks per thread are loaded before any is stored.
+  // exactly one item. With G = 1 the rows are read again from k / v (they were streamed as
+  // the item's last K/V tiles, so the reads mostly hit L2); eight 16-byte chunks per thread
+  // are loaded before any is stored.
   auto append_rows = [&](int q0i, int tid, int nthreads) {
     asm volatile("" : "+v"(tid));
     const int nrows = min(BMPOS, S - q0i);
@@ -613,11 +614,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     }
   };
 
-  // Output of one wave's 32 rows (O = O^T / l, bf16). The MFMA layout gives a lane 4
-  // consecutive dims of one row, so the tile is first written to 8 KiB of LDS at sbase (16-byte
-  // chunks XOR-swizzled by row % 16) and read back as whole rows, 16 lanes per 256-byte row:
-  // each global store then writes four complete rows instead of 16 bytes of each of 32 rows.
-  // rows 4i .. 4i+3 of a staged output tile to the output (rows of head h as a raw buffer, row
+  // Rows 4i .. 4i+3 of a staged output tile to the output (rows of head h as a raw buffer, row
   // i at byte i * Hq * ROWB; rows past the live ones get an offset beyond the buffer and the
   // hardware drops their stores)
   auto store_rows = [&](uint32_t sbase, int qa_e, int i) {
@@ -631,7 +628,11 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     const uint32_t off = row < n ? (uint32_t)row * q_stride + c * 16 : 0x80000000u;
     __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)off, 0, 0);
   };
-  // Stage this wave's output tile in LDS at sbase and, unless qa_e < 0, store it.
+  // Output of one wave's 32 rows (O = O^T / l, bf16). The MFMA layout gives a lane 4
+  // consecutive dims of one row, so the tile is first written to 8 KiB of LDS at sbase (16-byte
+  // chunks XOR-swizzled by row % 16) and read back as whole rows, 16 lanes per 256-byte row:
+  // each global store then writes four complete rows instead of 16 bytes of each of 32 rows.
+  // With qa_e < 0 the tile is only staged (stored later with store_rows).
   auto store_output = [&](uint32_t sbase, int qa_e) {
     const int ln = fresh_lane();
     const int rw = ln & 31, hf = ln >> 5;
