@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="extra lines for the split/batch sweeps")
+    ap.add_argument("--prefill-sweep", action="store_true",
+                    help="extra lines: causal prefill over sequence lengths and group sizes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -370,6 +372,34 @@ def main():
 
     if args.sweep:
         sweep(g, synth, dev, stream)
+    if args.prefill_sweep:
+        prefill_sweep(g, synth, dev, stream)
+
+
+def prefill_sweep(g, synth, dev, stream):
+    """Extra JSON lines: causal prefill (bf16, D=128, KV append included) over sequence lengths
+    at the benchmark's heads (Hq=32, Hkv=8; B*S = 8192 tokens) and over group sizes at S=2048
+    (Hq=32, Hkv = 32, 16, 8, 4; B=4). Median of 30 calls timed back to back with HIP events."""
+    shapes = [(16, 512, 32, 8), (8, 1024, 32, 8), (4, 2048, 32, 8), (2, 4096, 32, 8),
+              (1, 8192, 32, 8), (4, 2048, 32, 32), (4, 2048, 32, 16), (4, 2048, 32, 4)]
+    for B, S, hq, hkv in shapes:
+        p = synth.prefill_inputs(B, S, hq, hkv, 128, 16, seed=B * S + hkv, device=dev)
+        out = torch.empty_like(p.q)
+
+        def step():
+            g.prefill_causal(p.q, p.k, p.v, p.k_cache, p.v_cache, p.page_table, scale=p.scale,
+                             out=out)
+
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        med = statistics.median(event_times_queued(step, 30, stream))
+        fl = prefill_flops(B, S, hq, 128)
+        print(json.dumps({"prefill_sweep": f"B={B} S={S} Hq={hq} Hkv={hkv} G={hq // hkv}",
+                          "us": round(med * 1e3, 2),
+                          "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                          "frac": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}), flush=True)
+        del p, out
 
 
 def sweep(g, synth, dev, stream):
