@@ -494,9 +494,10 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // at the same time. Global phase p of an item: group A runs softmax(t) at p = 2t+1 and MFMA(t)
   // at p = 2t+2 (scores(0) at p = 0); group B runs one phase later. Hence K(t) is read in
   // phases 2t, 2t+1 and V(t) in phases 2t+2, 2t+3. Tile t >= 1 lives in stage t % 2 (K(0)
-  // in its own buffer); at every even phase 2u all waves issue the DMA of K(u+1) and V(u),
-  // whose stages were last read in phase 2u-1, and wait for it (vmcnt) before the barrier
-  // that opens phase 2u+2. At phase 2 * u_pf the waves also request the next item's Q rows
+  // in its own buffer); in every even phase 2u all waves issue the DMA of K(u+1) and V(u),
+  // whose stages were last read in phase 2u-1 (group A at the start of its MFMA phase, group
+  // B after its softmax, so that the two halves do not queue up together), and wait for it
+  // (vmcnt) before the barrier that opens phase 2u+2. At phase 2 * u_pf the waves also request the next item's Q rows
   // (8 loads per wave) and, for the causal prefill, the item's page ids (1 load), issued
   // after V(u_pf), so the wait before phase 2 * u_pf + 2 leaves those in flight: loads
   // complete in issue order. Every wave passes 2 * wg_tiles + 2 barriers per item.
@@ -546,8 +547,8 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     constexpr int PAR = decltype(par_tag)::value;
     wait_dma(t);
     bar();  // phase 2t+2
-    even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
     if (t < wave_tiles) softmax(t, t >= mask_from);
+    even_phase_dma(t + 1, std::integral_constant<int, PAR ^ 1>{});
     bar();  // phase 2t+3
     mfma_phase(t, par_tag);
   };
