@@ -1,5 +1,6 @@
 // extern "C" entry points of libgqa: validate on the host, then enqueue kernels on
 // the caller's stream. No allocation, no synchronisation, no global state.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include "../../include/gqa.h"
@@ -65,10 +66,21 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
   if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   char* data = (char*)workspace;
-  if (Hq / Hkv <= 8)
-    return gqa::launch_decode_balanced(q, k_cache, v_cache, page_table, context_lens, out, data, B,
-                                       Hq, Hkv, D, max_pages, scale, dtype, s);
-  const int ns = gqa_balanced_auto_splits(B, Hkv);
+  const int G = Hq / Hkv;
+  int ns = gqa_balanced_auto_splits(B, Hkv);
+  if (G <= 8) {
+    // Small problems (at most 1,024 (sequence, KV head, page) items, or 65,536 with one query
+    // head per KV head) run faster on the split path, with at least 16 pages per split, whose
+    // partials then fit in the slot area of the workspace; measured with T = 1024, Hq = 32 and
+    // B from 1 to 256.
+    const long items = (long)B * Hkv * max_pages;
+    const bool small = items <= (G == 1 ? 65536 : 1024);
+    ns = std::max(1, std::min(ns, max_pages / 16));
+    const size_t split_bytes = ns == 1 ? 0 : gqa_decode_workspace_bytes(B, Hq, D, ns);
+    if (!small || GQA_BALANCED_WS_RESERVED + split_bytes > workspace_bytes)
+      return gqa::launch_decode_balanced(q, k_cache, v_cache, page_table, context_lens, out, data,
+                                         B, Hq, Hkv, D, max_pages, scale, dtype, s);
+  }
   if (ns == 1)
     return gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
                                     nullptr, B, Hq, Hkv, D, max_pages, 1, scale, dtype, s);

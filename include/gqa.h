@@ -105,8 +105,9 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * resident wave; a (sequence, KV head) unit cut by a share boundary is finished from
  * its pieces with the log-sum-exp merge of gqa_combine_splits (the NumSplits
  * decomposition of page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
- * "核心参数调优：PackGQA与NumSplits的协同舞蹈"). For G >= 16 it runs the split path with
- * an automatic split count.
+ * "核心参数调优：PackGQA与NumSplits的协同舞蹈"). For G >= 16, and for small problems
+ * (B * Hkv * max_pages at most 1,024, or 65,536 when G = 1, if the split partials fit in the
+ * workspace past its counters) it runs the split path with an automatic split count.
  *
  *   workspace        device scratch of at least
  *                    gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D) bytes, 256-byte
@@ -117,7 +118,8 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *                    overlap in time.
  *   other arguments  as for gqa_decode_paged.
  * Enqueues one kernel on `stream` for G <= 8 (the pieces of units cut by the partition are
- * merged by the piece that finishes last); for G >= 16 the split decode + combine.
+ * merged by the piece that finishes last); on the split path the split decode and, with more
+ * than one split, the combine.
  */
 int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* page_table, const int32_t* context_lens, void* out,
