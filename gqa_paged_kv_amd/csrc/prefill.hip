@@ -404,35 +404,6 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     }
   };
 
-  // O^T += V^T P^T with V from stage ST (16 MFMAs, four chains), transpose reads issued
-  // PF MFMAs ahead.
-  auto pv = [&](auto st_tag) {
-    constexpr uint32_t SOFF = decltype(st_tag)::value * 2 * TILE;
-    constexpr int PF = 3;
-    auto vread = [&](int i) {  // operand of MFMA i = 4 sp + mbd
-      const int sp = i >> 2, mbd = i & 3;
-      const uint32_t a0p = voff[mbd] + SOFF + (16 * sp) * ROWB;
-      const s16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)a0p);
-      const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(a0p + 8 * ROWB));
-      const u32x2_t a0 = __builtin_bit_cast(u32x2_t, t0);
-      const u32x2_t a1 = __builtin_bit_cast(u32x2_t, t1);
-      return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-    };
-    u32x4_t va[PF + 1];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) va[i] = vread(i);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + PF < 16) va[(i + PF) % (PF + 1)] = vread(i + PF);
-      __builtin_amdgcn_sched_barrier(0);
-      oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8_t, va[i % (PF + 1)]),
-          __builtin_bit_cast(bf16x8_t, pop[i >> 2]), oacc[i & 3], 0, 0, 0);
-    }
-  };
-
   // One MFMA phase with both halves: PV of tile t (V from the stage of pv_tag) and the scores
   // of tile t+1 (K from the stage of sc_tag), their MFMAs interleaved one for one. The PV operands come from
   // transpose reads, which the LDS serves at about half the rate of the score loop's b128
