@@ -150,18 +150,17 @@ def decode_paged_rows(q, k_cache, v_cache, page_table, context_lens, scale: floa
     hkv = k_cache.shape[1]
     page_size = k_cache.shape[2]
     res = {}
-    cache_rows = {}
+    last_key, K, V = None, None, None  # rows of the last (b, kv head) gathered
     for (b, h) in rows:
         kvh = kv_head_of(h, hq, hkv)
         T = int(lens[b])
         if T == 0:
             res[(b, h)] = np.zeros(d)
             continue
-        key = (b, kvh)
-        if key not in cache_rows:
-            cache_rows[key] = (_gather_rows(k_cache, pt[b], T, kvh, page_size),
-                               _gather_rows(v_cache, pt[b], T, kvh, page_size))
-        K, V = cache_rows[key]
+        if (b, kvh) != last_key:
+            last_key = (b, kvh)
+            K = _gather_rows(k_cache, pt[b], T, kvh, page_size)
+            V = _gather_rows(v_cache, pt[b], T, kvh, page_size)
         qv = _f64(q[b, h])
         scores = scale * (K @ qv)
         res[(b, h)] = _softmax_weighted_sum(scores, V)

@@ -303,6 +303,20 @@ def test_append_round_trip_and_untouched_pages():
             assert torch.isnan(kc[p].float()).all()
 
 
+def test_kv_bytes_absolute():
+    """kv_bytes counts every cached K and V element once: workload 1's cache (2 sequences of
+    256 tokens, 2 KV heads, D = 64, fp32) is 2 * 512 * 2 * 64 * 4 = 524,288 bytes, and for any
+    shape it equals the byte size of a dense K tensor plus a dense V tensor [T][Hkv][D] of that
+    dtype."""
+    assert oracle.kv_bytes(2 * 256, 2, 64, 4) == 524_288
+    for T, hkv, d, dt in ((1, 1, 1, torch.bfloat16), (141_394, 8, 128, torch.bfloat16),
+                          (37, 3, 64, torch.float32), (1000, 32, 128, torch.uint8)):
+        k = torch.empty(T, hkv, d, dtype=dt)
+        v = torch.empty(T, hkv, d, dtype=dt)
+        dense = k.numel() * k.element_size() + v.numel() * v.element_size()
+        assert oracle.kv_bytes(T, hkv, d, k.element_size()) == dense
+
+
 def test_kv_size_ratio_golden():
     with open(os.path.join(GOLDEN, "kv_cache_ratio.json")) as f:
         g = json.load(f)
