@@ -42,6 +42,8 @@ SIGNATURES = {
     "gqa_validate_prefill_paged": (_i, [_p] * 9 + [_i] * 8 + [_f, _i]),
     "gqa_validate_combine": (_i, [_p, _p, _p, _i, _i, _i, _i, _i]),
     "gqa_gather_paged": (_i, [_p, _p, _p, _p] + [_i] * 7 + [_p]),
+    "gqa_decode_balanced_route": (_i, [_i, _i, _i, _i, _i, _sz]),
+    "gqa_check_page_table": (_i, [_p, _p, _i, _i, _i, _i]),
     "gqa_bench_stream_read": (_i, [_p, _sz, _p, _i, _i, _p]),
     "gqa_bench_mfma_bf16": (_i, [_p, _i, _i, _p]),
 }
@@ -152,14 +154,15 @@ def decode_paged(q, k_cache, v_cache, page_table, context_lens, num_splits: int 
     return out
 
 
-# Leading bytes of a balanced-decode workspace that hold counters (zero between calls).
-BALANCED_WS_RESERVED = 49152
+# Leading bytes of a balanced-decode workspace that hold counters (zero before first use;
+# every call tags them with a new epoch, so nothing needs clearing between calls).
+BALANCED_WS_RESERVED = 98304
 
 
 def balanced_workspace(B: int, Hq: int, Hkv: int, D: int, device):
     """Device scratch for decode_paged_balanced / decode_append / decode_paged_fp8 (uint8
-    tensor, 256-byte aligned, zero-filled: its leading counters must start at zero, and every
-    call leaves them zero, so the tensor can be reused across calls on one stream)."""
+    tensor, 256-byte aligned, zero-filled: its leading counters must start at zero; calls
+    tag them with increasing epochs, so the tensor can be reused by calls enqueued in order)."""
     n = int(load().gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D))
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
@@ -358,6 +361,28 @@ def gather_paged(cache, page_table, context_lens, dst=None):
                               _stream(cache.device))
     _check(st, "gqa_gather_paged")
     return dst
+
+
+def balanced_route(B: int, Hq: int, Hkv: int, D: int, max_pages: int,
+                   workspace_bytes: int | None = None) -> int:
+    """Route of decode_paged_balanced: 0 = persistent kernel, n >= 1 = split path with n splits
+    (host-only; workspace_bytes defaults to the size balanced_workspace allocates)."""
+    lib = load()
+    if workspace_bytes is None:
+        workspace_bytes = int(lib.gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D))
+    return int(lib.gqa_decode_balanced_route(B, Hq, Hkv, D, max_pages, workspace_bytes))
+
+
+def check_page_table(page_table, tokens, num_pages: int, page_size: int = 16) -> int:
+    """Host check of the page ids a call would touch (see gqa_check_page_table): page_table
+    [B][max_pages] and tokens [B] (int32, any device; copied to the host). Returns the status."""
+    pt = page_table.detach().to("cpu", torch.int32).contiguous()
+    tk = torch.as_tensor(tokens).detach().to("cpu", torch.int32).contiguous()
+    B, max_pages = pt.shape
+    if tk.shape != (B,):
+        raise ValueError("tokens must be [B]")
+    return int(load().gqa_check_page_table(_ptr(pt), _ptr(tk), B, max_pages, page_size,
+                                           num_pages))
 
 
 def bench_stream_read(src, sink, blocks_per_cu: int = 8, unroll: int = 8):

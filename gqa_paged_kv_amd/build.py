@@ -1,4 +1,5 @@
-"""Build libgqa.so (gfx950) in-tree with hipcc.
+"""Build libgqa.so (gfx950) in-tree with hipcc, and libgqa_debug.so: the same kernels with
+the entry points compiled with GQA_DEBUG (page ids checked on the host before every launch).
 
 Usage: python -m gqa_paged_kv_amd.build   (or gqa_paged_kv_amd.build.build())
 """
@@ -8,11 +9,13 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqa.so")
+DEBUG_LIB = os.path.join(HERE, "libgqa_debug.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["api.hip", "decode.hip", "decode_balanced.hip", "aux_kernels.hip", "prefill.hip",
@@ -44,7 +47,7 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in HIP_SOURCES + CPP_SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, src + ".o")
@@ -54,14 +57,26 @@ def build(verbose: bool = False) -> str:
             cmd = [hipcc, *HIPCC_FLAGS, "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        cmds.append(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    # the entry points once more with the debug page-id checks
+    dbg_obj = os.path.join(objdir, "api.hip.debug.o")
+    cmds.append([hipcc, *HIPCC_FLAGS, "-DGQA_DEBUG", "-c", os.path.join(CSRC, "api.hip"), "-o",
+                 dbg_obj])
+    # one compiler process per source, at most as many as the host has cores (and 8)
+    jobs = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(jobs) as pool:
+        for r in list(pool.map(lambda c: subprocess.run(c), cmds)):
+            if r.returncode != 0:
+                raise subprocess.CalledProcessError(r.returncode, r.args)
+    api_obj = os.path.join(objdir, "api.hip.o")
+    for lib, lib_objs in ((LIB, objs), (DEBUG_LIB, [dbg_obj if o == api_obj else o for o in objs])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

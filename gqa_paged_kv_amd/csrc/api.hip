@@ -1,5 +1,6 @@
 // extern "C" entry points of libgqa: validate on the host, then enqueue kernels on
-// the caller's stream. No allocation, no synchronisation, no global state.
+// the caller's stream. No allocation and no synchronisation (a build with GQA_DEBUG defined
+// checks page ids on the host first, which synchronises the stream).
 #include <algorithm>
 #include <hip/hip_runtime.h>
 
@@ -35,7 +36,48 @@ int launch_prefill_paged(const void* q, const void* k, const void* v, void* out,
                          int D, float scale, hipStream_t s);
 }  // namespace gqa
 
-extern "C" int gqa_balanced_auto_splits(int B, int Hkv);
+
+#ifdef GQA_DEBUG
+#include <vector>
+// Debug build: before anything is enqueued, the page table and the per-sequence lengths are
+// copied to the host (after the work already queued on `stream`, which may have written
+// them) and every page id the call would touch is checked against the pool by
+// gqa_check_page_table. kind 0: decode over lens[b] tokens; 1: decode with the step's token
+// appended (lens[b] clamped to max_pages * P - 1, plus one); 2: prefill of S tokens per
+// sequence; 3: chunked prefill, past (lens) plus new (lens2) tokens.
+namespace {
+int debug_check_pages(const int32_t* pt, const int32_t* lens, const int32_t* lens2, int kind,
+                      int S, int B, int max_pages, int P, int num_pages, hipStream_t s) {
+  std::vector<int32_t> h_pt((size_t)B * max_pages), a(B, 0), n(B, 0), tok(B, 0);
+  if (hipMemcpyAsync(h_pt.data(), pt, h_pt.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return GQA_ERR_LAUNCH;
+  if (lens && hipMemcpyAsync(a.data(), lens, (size_t)B * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return GQA_ERR_LAUNCH;
+  if (lens2 && hipMemcpyAsync(n.data(), lens2, (size_t)B * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return GQA_ERR_LAUNCH;
+  if (hipStreamSynchronize(s) != hipSuccess) return GQA_ERR_LAUNCH;
+  const int cap = max_pages * P;
+  for (int b = 0; b < B; ++b) {
+    const int t = std::min(std::max(a[b], 0), cap);
+    if (kind == 0) tok[b] = t;
+    if (kind == 1) tok[b] = std::min(std::max(a[b], 0), cap - 1) + 1;
+    if (kind == 2) tok[b] = S;
+    if (kind == 3) tok[b] = t + std::min(std::max(n[b], 0), std::min(S, cap - t));
+  }
+  return gqa_check_page_table(h_pt.data(), tok.data(), B, max_pages, P, num_pages);
+}
+}  // namespace
+#define GQA_DEBUG_CHECK_PAGES(pt, lens, lens2, kind, S, B, mp, P, np, stream)                   \
+  do {                                                                                          \
+    const int st_ = debug_check_pages(pt, lens, lens2, kind, S, B, mp, P, np,                   \
+                                      (hipStream_t)(stream));                                   \
+    if (st_ != GQA_OK) return st_;                                                              \
+  } while (0)
+#else
+#define GQA_DEBUG_CHECK_PAGES(pt, lens, lens2, kind, S, B, mp, P, np, stream) \
+  do {                                                                       \
+  } while (0)
+#endif
 
 extern "C" {
 
@@ -47,6 +89,7 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
                                B, Hq, Hkv, D, P, max_pages, num_pages, num_splits, scale, dtype);
   if (st != GQA_OK) return st;
+  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 0, 0, B, max_pages, P, num_pages, stream);
   hipStream_t s = (hipStream_t)stream;
   st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
                                 B, Hq, Hkv, D, max_pages, num_splits, scale, dtype, s);
@@ -64,27 +107,17 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
   if (st != GQA_OK) return st;
   if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
   if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
+  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 0, 0, B, max_pages, P, num_pages, stream);
   hipStream_t s = (hipStream_t)stream;
   char* data = (char*)workspace;
-  const int G = Hq / Hkv;
-  int ns = gqa_balanced_auto_splits(B, Hkv);
-  if (G <= 8) {
-    // Small problems (at most 1,024 (sequence, KV head, page) items, or 65,536 with one query
-    // head per KV head) run faster on the split path, with at least 16 pages per split, whose
-    // partials then fit in the slot area of the workspace; measured with T = 1024, Hq = 32 and
-    // B from 1 to 256.
-    const long items = (long)B * Hkv * max_pages;
-    const bool small = items <= (G == 1 ? 65536 : 1024);
-    ns = std::max(1, std::min(ns, max_pages / 16));
-    const size_t split_bytes = ns == 1 ? 0 : gqa_decode_workspace_bytes(B, Hq, D, ns);
-    if (!small || GQA_BALANCED_WS_RESERVED + split_bytes > workspace_bytes)
-      return gqa::launch_decode_balanced(q, k_cache, v_cache, page_table, context_lens, out, data,
-                                         B, Hq, Hkv, D, max_pages, scale, dtype, s);
-  }
+  const int ns = gqa_decode_balanced_route(B, Hq, Hkv, D, max_pages, workspace_bytes);
+  if (ns == 0)
+    return gqa::launch_decode_balanced(q, k_cache, v_cache, page_table, context_lens, out, data,
+                                       B, Hq, Hkv, D, max_pages, scale, dtype, s);
   if (ns == 1)
     return gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
                                     nullptr, B, Hq, Hkv, D, max_pages, 1, scale, dtype, s);
-  // the split partials start past the persistent path's counters, which stay zero
+  // the split partials start past the persistent path's counters
   float* ws_o = (float*)(data + GQA_BALANCED_WS_RESERVED);
   float* ws_lse = ws_o + (size_t)B * Hq * ns * D;
   st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
@@ -105,6 +138,7 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   if (Hq / Hkv > 8) return GQA_ERR_UNSUPPORTED;
   if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
   if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
+  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 1, 0, B, max_pages, P, num_pages, stream);
   return gqa::launch_decode_append(q, k_new, v_new, k_cache, v_cache, page_table, context_lens,
                                    out, workspace, B, Hq, Hkv, D, max_pages, scale, dtype,
                                    (hipStream_t)stream);
@@ -121,6 +155,7 @@ int gqa_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache
   if (st != GQA_OK) return st;
   if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
   if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
+  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 0, 0, B, max_pages, P, num_pages, stream);
   return gqa::launch_decode_balanced_fp8(q, k_cache, v_cache, k_scale, v_scale, page_table,
                                          context_lens, out, workspace, B, Hq, Hkv, D, max_pages,
                                          scale, kv_dtype, (hipStream_t)stream);
@@ -141,6 +176,7 @@ int gqa_prefill_causal(const void* q, const void* k, const void* v, void* k_cach
   int st = gqa_validate_prefill(q, k, v, k_cache, v_cache, page_table, out, B, S, Hq, Hkv, D, P,
                                 max_pages, num_pages, scale, dtype);
   if (st != GQA_OK) return st;
+  GQA_DEBUG_CHECK_PAGES(page_table, nullptr, nullptr, 2, S, B, max_pages, P, num_pages, stream);
   // one kernel: attention plus the append of the new K/V rows into the cache
   return gqa::launch_prefill(q, k, v, out, k_cache, v_cache, page_table, max_pages, B, S, Hq, Hkv,
                              D, scale, (hipStream_t)stream);
@@ -153,6 +189,7 @@ int gqa_prefill_paged(const void* q, const void* k, const void* v, void* k_cache
   int st = gqa_validate_prefill_paged(q, k, v, k_cache, v_cache, page_table, past_lens, new_lens,
                                       out, B, S, Hq, Hkv, D, P, max_pages, num_pages, scale, dtype);
   if (st != GQA_OK) return st;
+  GQA_DEBUG_CHECK_PAGES(page_table, past_lens, new_lens, 3, S, B, max_pages, P, num_pages, stream);
   return gqa::launch_prefill_paged(q, k, v, out, k_cache, v_cache, page_table, past_lens, new_lens,
                                    max_pages, B, S, Hq, Hkv, D, scale, (hipStream_t)stream);
 }
@@ -165,6 +202,7 @@ int gqa_gather_paged(const void* cache, const int32_t* page_table, const int32_t
     return GQA_ERR_INVALID_ARG;
   if (dtype != GQA_F32 && dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
   if ((D != 64 && D != 128) || P != 16 || B > 65535) return GQA_ERR_UNSUPPORTED;
+  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 0, 0, B, max_pages, P, num_pages, stream);
   return gqa::launch_gather(cache, page_table, context_lens, dst, B, Hkv, D, P, max_pages, dtype,
                             (hipStream_t)stream);
 }

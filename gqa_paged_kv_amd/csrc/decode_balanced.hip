@@ -18,9 +18,9 @@
 // piece, a partial (normalised output + natural-log LSE) in the share's slot 0 (its first
 // unit) or slot 1 (its last unit), written with device-coherent write-through stores of
 // whole 128-byte lines. After its last page a wave counts its pieces on per-group /
-// per-unit counters (device-scope atomics); the piece that completes a count merges (a
-// group of up to kGroup pieces, then the group partials of a long unit) and clears the
-// counter, so no second launch and no cache flush is needed. Each wave keeps pages in
+// per-unit counters (device-scope atomics, tagged with the call's epoch); the piece that
+// completes a count merges (a group of up to kGroup pieces, then the group partials of a long
+// unit), so no second launch and no cache flush is needed. Each wave keeps pages in
 // flight in VGPRs while it computes one; all G <= 8 heads of the group live in the wave,
 // so a K/V row is read once. Rows of sequences with T_b = 0 are zero-filled.
 #include <atomic>
@@ -32,11 +32,17 @@ namespace gqa {
 
 constexpr int kBalancedMaxWaves = 4096;  // upper bound of the persistent grid (workspace size)
 
-// Workspace: GQA_BALANCED_WS_RESERVED bytes of counters (kBalancedMaxWaves per-unit counters,
-// then 2 kBalancedMaxWaves per-group counters; zero between calls), then kBalancedMaxWaves x 2
-// partial slots of SlotGeom::FLOATS floats (whole 128-byte lines).
+// Workspace: GQA_BALANCED_WS_RESERVED bytes of 64-bit counters (kBalancedMaxWaves per-unit
+// counters, then 2 kBalancedMaxWaves per-group counters), then kBalancedMaxWaves x 2 partial
+// slots of SlotGeom::FLOATS floats (whole 128-byte lines). A counter holds
+// (epoch << kEpochShift) + count: every call takes a new, larger epoch from the host, and a
+// piece first raises the counter to its call's base (atomic max), then counts on it (atomic
+// add), so whatever an earlier call left in a counter (a finished call's full count, or the
+// partial count of a call that never completed) is discarded by the next call. The counters
+// must hold zero (or any earlier epoch's value) before the first call on a workspace.
 constexpr int kGroup = 8;  // pieces merged together at the first level
-static_assert(GQA_BALANCED_WS_RESERVED == 3 * kBalancedMaxWaves * 4, "counter region");
+constexpr int kEpochShift = 16;  // counts stay below 2^16 (at most kBalancedMaxWaves pieces)
+static_assert(GQA_BALANCED_WS_RESERVED == 3 * kBalancedMaxWaves * 8, "counter region");
 
 // Partial slot of one piece: the G x D normalised output as 16-byte chunks, chunk i * 64 +
 // lane holding pair k = 4 i + lane / 16 (head k / JPH, chunk k % JPH of that head's E dims
@@ -295,8 +301,9 @@ template <typename T, int D, int G, typename TKV = T, bool APPEND = false>
 __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     const T* __restrict__ q, const TKV* __restrict__ k_cache, const TKV* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ context_lens,
-    T* __restrict__ out, float* __restrict__ slots, int* __restrict__ counters, int B, int Hq,
-    int Hkv, int max_pages, float scale_log2, float out_scale, const TKV* __restrict__ k_new,
+    T* __restrict__ out, float* __restrict__ slots, unsigned long long* __restrict__ counters,
+    unsigned long long epoch_base, int B, int Hq, int Hkv, int max_pages, float scale_log2,
+    float out_scale, const TKV* __restrict__ k_new,
     const TKV* __restrict__ v_new, TKV* __restrict__ k_store, TKV* __restrict__ v_store) {
   using S = DecodeShape<TKV, D, G>;
   constexpr int append = APPEND ? 1 : 0;
@@ -511,21 +518,23 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   // counted. Units of up to kGroup pieces: the piece that completes its group's count
   // merges the unit into the output. Longer units: the last piece of each group of kGroup
   // consecutive pieces merges the group into a partial (in the group's first slot) and
-  // counts it on the unit's counter; the last group merges the group partials. Whoever
-  // completes a count clears that counter for the next call.
+  // counts it on the unit's counter; the last group merges the group partials.
   if ((piece0.valid | piece1.valid) == 0) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  int* const unit_cnt = counters;
-  int* const group_cnt = counters + kBalancedMaxWaves;
-  auto count_in = [&](int* c) {
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = uniform(old);
+  unsigned long long* const unit_cnt = counters;
+  unsigned long long* const group_cnt = counters + kBalancedMaxWaves;
+  // This piece's arrival number on counter c within this call (1 = first). Both atomics act
+  // on one address from one lane, so they take effect in program order (the language's
+  // coherence rule for one object).
+  auto count_in = [&](unsigned long long* c) {
+    unsigned long long old = 0;
+    if (lane == 0) {
+      __hip_atomic_fetch_max(c, epoch_base, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old = (unsigned long long)uniform((long)old);
     asm volatile("" ::: "memory");
-    return old + 1;
-  };
-  auto clear = [&](int* c) {
-    if (lane == 0) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (long)(old + 1 - epoch_base);
   };
   auto publish = [&](const Piece& pc) {
     const int w0 = share_owner(N, pc.first, nw);
@@ -536,9 +545,8 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     const int gfirst = w0 + g * kGroup;
     const int gsize = min(kGroup, npc - g * kGroup);
     const int ngroups = (npc + kGroup - 1) / kGroup;
-    int* gc = group_cnt + 2 * gfirst + (g == 0 ? s0 : 0);
+    unsigned long long* gc = group_cnt + 2 * gfirst + (g == 0 ? s0 : 0);
     if (count_in(gc) != gsize) return;  // another piece of the group is still running
-    clear(gc);
     auto piece_off = [&](int p) { return slot_off(gfirst + p, (g == 0 && p == 0) ? s0 : 0); };
     if (ngroups == 1) {
       merge_pieces<T, D, G, true>(rs, gsize, piece_off, out + pc.dst, 0u, lane);
@@ -546,9 +554,8 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     }
     merge_pieces<T, D, G, false>(rs, gsize, piece_off, out, piece_off(0), lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    int* uc = unit_cnt + w0;
+    unsigned long long* uc = unit_cnt + w0;
     if (count_in(uc) != ngroups) return;
-    clear(uc);
     auto group_off = [&](int gg) { return slot_off(w0 + gg * kGroup, gg == 0 ? s0 : 0); };
     merge_pieces<T, D, G, true>(rs, ngroups, group_off, out + pc.dst, 0u, lane);
   };
@@ -557,6 +564,14 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
 }
 
 // ---- host side --------------------------------------------------------------------------
+
+// Epoch of the next call, shifted into place: a process-wide count of launches of the
+// balanced kernel, so every call on a workspace sees a larger epoch than the calls enqueued
+// before it (calls that share a workspace are enqueued in order from one thread at a time).
+static unsigned long long next_epoch_base() {
+  static std::atomic<unsigned long long> epoch{0};
+  return (epoch.fetch_add(1, std::memory_order_relaxed) + 1) << kEpochShift;
+}
 
 template <typename T, int D, int G, typename TKV = T, bool APPEND = false>
 static int launch_balanced(const void* q, const void* k, const void* v, const int32_t* pt,
@@ -582,11 +597,12 @@ static int launch_balanced(const void* q, const void* k, const void* v, const in
     if (grid * kDecodeWaves > kBalancedMaxWaves) grid = kBalancedMaxWaves / kDecodeWaves;
     grid_cache[dev].store(grid, std::memory_order_relaxed);
   }
-  int* counters = (int*)slots_ws;
+  unsigned long long* counters = (unsigned long long*)slots_ws;
   float* slots = (float*)((char*)slots_ws + GQA_BALANCED_WS_RESERVED);
   hipLaunchKernelGGL((balanced_kernel<T, D, G, TKV, APPEND>), dim3(grid), dim3(kDecodeThreads), 0, s,
                      (const T*)q, (const TKV*)k, (const TKV*)v, pt, lens, (T*)out, slots, counters,
-                     B, Hq, Hkv, max_pages, scale * kLog2e, out_scale, (const TKV*)k_new,
+                     next_epoch_base(), B, Hq, Hkv, max_pages, scale * kLog2e, out_scale,
+                     (const TKV*)k_new,
                      (const TKV*)v_new, (TKV*)k_store, (TKV*)v_store);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }

@@ -77,29 +77,83 @@ int gqa_validate_decode(const void* q, const void* k_cache, const void* v_cache,
   return GQA_OK;
 }
 
-// Split count used by the balanced entry point when G >= 16 (the LDS-staged split path,
-// one workgroup per (sequence, KV head, split)): enough splits for one workgroup per CU of
-// the 256-CU MI355X and no more. Measured with B x Hkv from 1 to 256 (Hq = 32, T = 1024):
-// fewer splits leave CUs idle, more add combine traffic and shorter per-split streams.
-int gqa_balanced_auto_splits(int B, int Hkv) {
+}  // extern "C"
+
+namespace {
+
+// Split count of the split path when the balanced entry point takes it: enough splits for
+// one workgroup per CU of the 256-CU MI355X and no more (measured with B x Hkv from 1 to 256,
+// Hq = 32, T = 1024: fewer splits leave CUs idle, more add combine traffic and shorter
+// per-split streams).
+int auto_splits(int B, int Hkv) {
   const long units = (long)B * Hkv;
   if (units <= 0) return 1;
   long ns = (256 + units - 1) / units;
   return (int)(ns < 1 ? 1 : (ns > 16 ? 16 : ns));
 }
 
-// Workspace of the balanced entry point: per-wave partial slots (G <= 8) or the split
-// partials (G >= 16).
+// Bytes of the persistent path's partial slots: 4096 waves x 2 slots of G x D + G floats
+// rounded up to whole 128-byte lines.
+size_t slot_area_bytes(int G, int D) {
+  if (G > 8) return 0;
+  const size_t slot_floats = ((size_t)G * D + G + 31) / 32 * 32;
+  return (size_t)4096 * 2 * slot_floats * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Route of the balanced entry point. G <= 8: the persistent kernel, except for small problems
+// (at most 1,024 (sequence, KV head, page) items, or 65,536 with one query head per KV head),
+// which run faster on the split path with at least 16 pages per split (measured with
+// T = 1024, Hq = 32 and B from 1 to 256) provided its partials fit in the workspace past the
+// counters. G >= 16: the split path with auto_splits splits.
+int gqa_decode_balanced_route(int B, int Hq, int Hkv, int D, int max_pages,
+                              size_t workspace_bytes) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_pages <= 0 || Hq % Hkv != 0) return -1;
+  const int G = Hq / Hkv;
+  int ns = auto_splits(B, Hkv);
+  if (G <= 8) {
+    const long items = (long)B * Hkv * max_pages;
+    const bool small = items <= (G == 1 ? 65536 : 1024);
+    ns = max_pages / 16 < ns ? max_pages / 16 : ns;
+    if (ns < 1) ns = 1;
+    const size_t split_bytes = ns == 1 ? 0 : gqa_decode_workspace_bytes(B, Hq, D, ns);
+    if (!small || GQA_BALANCED_WS_RESERVED + split_bytes > workspace_bytes) return 0;
+  }
+  return ns;
+}
+
+// Workspace of the balanced entry point: counters, then per-wave partial slots (G <= 8) or
+// the split partials (G >= 16).
 size_t gqa_decode_balanced_workspace_bytes(int B, int Hq, int Hkv, int D) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
-  const size_t G = (size_t)(Hq / Hkv);
-  // counters (zero between calls), then either the persistent path's 4096 waves x 2 slots
-  // of G x D + G floats rounded up to whole 128-byte lines, or the split path's partials
-  const size_t slot_floats = (G * D + G + 31) / 32 * 32;
-  const size_t slot_bytes = G <= 8 ? (size_t)4096 * 2 * slot_floats * sizeof(float) : 0;
-  const size_t split_bytes =
-      G >= 16 ? gqa_decode_workspace_bytes(B, Hq, D, gqa_balanced_auto_splits(B, Hkv)) : 0;
+  const int G = Hq / Hkv;
+  const size_t slot_bytes = slot_area_bytes(G, D);
+  const int ns = auto_splits(B, Hkv);
+  const size_t split_bytes = G >= 16 && ns > 1 ? gqa_decode_workspace_bytes(B, Hq, D, ns) : 0;
   return GQA_BALANCED_WS_RESERVED + (slot_bytes > split_bytes ? slot_bytes : split_bytes);
+}
+
+// Page ids that a call would read or write, checked against the pool on the host: for every
+// sequence the first ceil(tokens[b] / P) entries of its row (tokens clamped to
+// [0, max_pages * P]) must lie in [0, num_pages).
+int gqa_check_page_table(const int32_t* page_table, const int32_t* tokens, int B,
+                         int max_pages, int P, int num_pages) {
+  if (!page_table || !tokens) return GQA_ERR_INVALID_ARG;
+  if (B <= 0 || max_pages <= 0 || P <= 0 || num_pages <= 0) return GQA_ERR_INVALID_ARG;
+  if ((int64_t)max_pages * P > INT32_MAX) return GQA_ERR_INVALID_ARG;
+  const int cap = max_pages * P;
+  for (int b = 0; b < B; ++b) {
+    int t = tokens[b];
+    t = t < 0 ? 0 : (t > cap ? cap : t);
+    const int np = (t + P - 1) / P;
+    const int32_t* row = page_table + (size_t)b * max_pages;
+    for (int i = 0; i < np; ++i)
+      if (row[i] < 0 || row[i] >= num_pages) return GQA_ERR_INVALID_ARG;
+  }
+  return GQA_OK;
 }
 
 int gqa_validate_prefill(const void* q, const void* k, const void* v, const void* k_cache,

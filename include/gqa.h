@@ -21,8 +21,13 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer is a DEVICE pointer owned by the caller. The library never
- *     allocates, frees or synchronises, and keeps no state between calls, so
- *     calls from several host threads are safe.
+ *     allocates, frees or synchronises (a build with GQA_DEBUG defined
+ *     synchronises the stream to check page ids, see gqa_check_page_table).
+ *     Its only state is process-wide and thread-safe: a per-device cache of
+ *     the persistent decode grid (an occupancy query made on the first call on
+ *     each device) and the epoch counter of the balanced-decode workspaces.
+ *     Calls from several host threads are safe when they use different
+ *     workspaces.
  *   - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the default stream) and runs asynchronously; the return value reports
  *     host-side argument validation and the launch only. A device fault (for
@@ -54,9 +59,11 @@ typedef enum {
   GQA_ERR_LAUNCH = 3       /* the HIP runtime refused the kernel launch */
 } gqa_status;
 
-/* Bytes at the start of a balanced-decode workspace that hold counters: they must be zero
- * before the first call that uses the workspace, and every call leaves them zero. */
-#define GQA_BALANCED_WS_RESERVED 49152
+/* Bytes at the start of a balanced-decode workspace that hold 64-bit counters. They must be
+ * zero before the first call that uses the workspace; every call then tags them with a new
+ * epoch, so they need no clearing between calls, and a call that never completed leaves
+ * nothing that a later call would count. */
+#define GQA_BALANCED_WS_RESERVED 98304
 
 typedef enum {
   GQA_F32 = 0,
@@ -107,15 +114,19 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * decomposition of page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
  * "核心参数调优：PackGQA与NumSplits的协同舞蹈"). For G >= 16, and for small problems
  * (B * Hkv * max_pages at most 1,024, or 65,536 when G = 1, if the split partials fit in the
- * workspace past its counters) it runs the split path with an automatic split count.
+ * workspace past its counters) it runs the split path with an automatic split count; see
+ * gqa_decode_balanced_route. The route depends on the page-table row width max_pages, not
+ * on the live lengths: a table sized for a long maximum context always takes the persistent
+ * kernel.
  *
  *   workspace        device scratch of at least
  *                    gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D) bytes, 256-byte
  *                    aligned, owned by the caller. Zero it once after allocating it: its
- *                    first GQA_BALANCED_WS_RESERVED bytes are counters that every call
- *                    leaves at zero (the rest is overwritten). One workspace serves every
- *                    shape whose size it covers. Calls that share a workspace must not
- *                    overlap in time.
+ *                    first GQA_BALANCED_WS_RESERVED bytes are counters, tagged by every
+ *                    call with a new epoch (the rest is overwritten). One workspace serves
+ *                    every shape whose size it covers. Calls that share a workspace must
+ *                    not overlap in time and must be enqueued in order (from one host
+ *                    thread at a time).
  *   other arguments  as for gqa_decode_paged.
  * Enqueues one kernel on `stream` for G <= 8 (the pieces of units cut by the partition are
  * merged by the piece that finishes last); on the split path the split decode and, with more
@@ -229,15 +240,38 @@ int gqa_prefill_paged(const void* q, const void* k, const void* v, void* k_cache
                       int P, int max_pages, int num_pages, float scale, int dtype, void* stream);
 
 /*
- * Merge split partials: M = max_s lse_s, w_s = exp(lse_s - M),
- * out = sum_s w_s o_s / sum_s w_s; a row whose splits are all -inf is zero.
+ * Merge split partials, the last step of the NumSplits decomposition (page
+ * "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
+ * "核心参数调优：PackGQA与NumSplits的协同舞蹈": the attention of one query is cut
+ * into sub-problems over parts of the context, and their results are combined):
+ * M = max_s lse_s, w_s = exp(lse_s - M), out = sum_s w_s o_s / sum_s w_s; a row
+ * whose splits are all -inf is zero.
  *   ws_o [B][Hq][num_splits][D] fp32, ws_lse [B][Hq][num_splits] fp32
  *   (natural log), out [B][Hq][D] in out_dtype.
+ * Returns GQA_OK, or an error code with nothing enqueued.
  */
 int gqa_combine_splits(const float* ws_o, const float* ws_lse, void* out, int B, int Hq, int D,
                        int num_splits, int out_dtype, void* stream);
 
 /* Host-only helpers (no GPU access). */
+
+/* Route gqa_decode_paged_balanced takes for a shape and workspace size: 0 = the persistent
+ * balanced kernel (one launch); n >= 1 = the split path with n splits (n > 1 adds the
+ * combine). -1 if the arguments are invalid. */
+int gqa_decode_balanced_route(int B, int Hq, int Hkv, int D, int max_pages,
+                              size_t workspace_bytes);
+
+/* Page ids a call would touch, checked on the host: page_table [B][max_pages] and tokens [B]
+ * are HOST arrays; for every b the first ceil(t_b / P) entries of row b, with t_b = tokens[b]
+ * clamped to [0, max_pages * P], must lie in [0, num_pages). The token count is what the call
+ * reads or writes: context_lens[b] for decode, context_lens[b] + 1 for gqa_decode_append, S
+ * for causal prefill, past + new for chunked prefill. Returns GQA_OK or
+ * GQA_ERR_INVALID_ARG (also for null arrays or non-positive sizes). Page ids outside the pool
+ * are a caller error that the kernels do not check; a library built with GQA_DEBUG defined
+ * runs this check in every entry point (after a blocking copy of the table and lengths) and
+ * returns its status before enqueueing anything. */
+int gqa_check_page_table(const int32_t* page_table, const int32_t* tokens, int B,
+                         int max_pages, int P, int num_pages);
 size_t gqa_decode_workspace_bytes(int B, int Hq, int D, int num_splits); /* ws_o + ws_lse */
 size_t gqa_decode_balanced_workspace_bytes(int B, int Hq, int Hkv, int D);  /* 0 if invalid */
 const char* gqa_status_string(int status);
@@ -264,11 +298,16 @@ int gqa_validate_combine(const float* ws_o, const float* ws_lse, const void* out
                          int D, int num_splits, int out_dtype);
 
 /*
- * Test-only: copy the live tokens of a paged cache to a contiguous buffer,
+ * Test-only: copy the live tokens of a paged cache to a contiguous buffer through
+ * the logical -> physical page mapping (page "TensorRT对Grouped Query Attention的支持
+ * 进展", section "动态形状与KV Cache管理": the caller passes physical page ids and
+ * logical positions are mapped to them; page "TensorRT-LLM与TensorRT核心差异解析",
+ * section 4.2.2: a page table maps logically contiguous tokens to scattered
+ * fixed-size pages):
  * dst[b][t][kvh][:] = cache[page_table[b][t / P]][kvh][t % P][:] for
  * t < min(context_lens[b], max_pages*P); dst is [B][max_pages*P][Hkv][D] and
  * rows t >= T_b are left untouched. Bit-exact copy of the indexing that the
- * attention kernels use.
+ * attention kernels use. Returns GQA_OK, or an error code with nothing enqueued.
  */
 int gqa_gather_paged(const void* cache, const int32_t* page_table, const int32_t* context_lens,
                      void* dst, int B, int Hkv, int D, int P, int max_pages, int num_pages,

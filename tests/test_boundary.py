@@ -64,7 +64,7 @@ def test_balanced_workspace_layout(lib):
     path's slots (whole 128-byte lines per piece) and the split path's partials."""
     text = open(os.path.join(ROOT, "include", "gqa.h")).read()
     m = re.search(r"#define\s+GQA_BALANCED_WS_RESERVED\s+(\d+)", text)
-    assert m and int(m.group(1)) == g.BALANCED_WS_RESERVED == 3 * 4096 * 4
+    assert m and int(m.group(1)) == g.BALANCED_WS_RESERVED == 3 * 4096 * 8  # 64-bit counters
     n = lib.gqa_decode_balanced_workspace_bytes
     slot_floats = (4 * 128 + 4 + 31) // 32 * 32  # G = 4, D = 128
     assert n(64, 32, 8, 128) == g.BALANCED_WS_RESERVED + 4096 * 2 * slot_floats * 4
@@ -72,6 +72,53 @@ def test_balanced_workspace_layout(lib):
     assert n(0, 32, 8, 128) == 0 and n(4, 30, 8, 128) == 0
     # G >= 16 takes the split path: counters, then its partials only
     assert n(8, 32, 1, 128) == g.BALANCED_WS_RESERVED + g.workspace_bytes(8, 32, 128, 16)  # NS = 16
+    assert n(256, 32, 1, 128) == g.BALANCED_WS_RESERVED  # one split: no partials
+
+
+def test_balanced_route_limits(lib):
+    """The balanced entry point's route: the persistent kernel (0) above 1,024 (sequence, KV
+    head, page) items (65,536 for G = 1), the split path (n >= 1 splits) at or below, the split
+    path for G >= 16 at every size, and the persistent kernel whenever the split partials
+    would not fit in the workspace."""
+    r = g.balanced_route
+    # G = 4: B * Hkv * max_pages = 1024 / 1025
+    assert r(2, 32, 8, 128, 64) >= 1 and r(2, 32, 8, 128, 64) == min(256 // 16, 64 // 16)
+    assert r(1, 32, 8, 128, 128) >= 1 and r(1, 32, 8, 128, 129) == 0
+    assert r(5, 20, 5, 128, 41) == 0 and r(5, 20, 5, 128, 40) >= 1  # 1025 vs 1000 items
+    # G = 1: 65536 / 65537 items
+    assert r(8, 8, 8, 128, 1024) >= 1 and r(8, 8, 8, 128, 1025) == 0
+    assert r(1, 1, 1, 128, 65536) >= 1 and r(1, 1, 1, 128, 65537) == 0
+    # G = 8 and G = 2 follow the 1,024 rule
+    assert r(4, 32, 4, 64, 64) >= 1 and r(4, 32, 4, 64, 65) == 0
+    assert r(1, 32, 16, 128, 64) >= 1 and r(1, 32, 16, 128, 65) == 0
+    # narrow tables: at least 16 pages per split, so fewer than 32 pages means one split
+    assert r(2, 8, 2, 128, 16) == 1 and r(2, 8, 2, 128, 31) == 1 and r(2, 8, 2, 128, 32) == 2
+    # a workspace that holds only the counters keeps small problems on the persistent kernel
+    assert r(2, 32, 8, 128, 64, g.BALANCED_WS_RESERVED) == 0
+    # G >= 16: always the split path, one workgroup per CU (at most 16 splits)
+    for B, hkv, ns in ((1, 1, 16), (8, 1, 16), (32, 1, 8), (64, 1, 4), (256, 1, 1), (64, 2, 2)):
+        assert r(B, 32, hkv, 128, 64) == ns, (B, hkv)
+        assert r(B, 32, hkv, 128, 100000) == ns, (B, hkv)
+    assert r(0, 32, 8, 128, 64) == -1 and r(2, 30, 8, 128, 64) == -1
+
+
+def test_page_table_check(lib):
+    """gqa_check_page_table: every page id a call touches must lie in [0, num_pages); entries
+    past ceil(tokens / P) are never looked at; tokens are clamped to the row width."""
+    import torch
+    pt = torch.tensor([[3, 0, -1, 99], [1, 2, 5, 7]], dtype=torch.int32)
+    chk = lambda tok, n=8: g.check_page_table(pt, torch.tensor(tok, dtype=torch.int32), n)
+    assert chk([32, 64]) == g.OK            # row 0: pages 3, 0; row 1: all four < 8
+    assert chk([33, 64]) == g.ERR_INVALID_ARG  # row 0 reaches the -1 entry
+    assert chk([0, 48]) == g.OK
+    assert chk([-5, 48]) == g.OK            # negative lengths touch nothing
+    assert chk([32, 64], n=7) == g.ERR_INVALID_ARG  # page 7 outside a 7-page pool
+    assert chk([32, 10**6], n=8) == g.OK    # clamped to max_pages * P = 64
+    assert chk([10**6, 0]) == g.ERR_INVALID_ARG  # clamped: row 0 reaches -1 and 99
+    pt[0, 2], pt[0, 3] = 4, 8
+    assert chk([64, 0]) == g.ERR_INVALID_ARG  # 8 == num_pages is outside
+    assert chk([64, 0], n=9) == g.OK
+    assert lib.gqa_check_page_table(None, None, 2, 4, 16, 8) == g.ERR_INVALID_ARG
 
 
 def _vd(lib, **kw):
