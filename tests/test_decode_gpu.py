@@ -171,20 +171,16 @@ def test_config4_long_context_splits(gpu_lib, B):
 
 @pytest.mark.parametrize("Hkv", synth.CONFIG5_KV_HEADS)
 @pytest.mark.parametrize("B", synth.CONFIG5_BATCHES)
-def test_config5_sweep(gpu_lib, B, Hkv):
+def test_config5_sweep_whole_output(gpu_lib, B, Hkv):
+    """Every (B, Hkv) point of the batch/group sweep: all B x 32 output rows against the
+    float64 oracle, on the split path (one split) and through the balanced entry point (the
+    route the benchmark times)."""
     print(f"[decode] config5 B={B} Hkv={Hkv}", flush=True)
     x = synth.config5(B, Hkv, device=DEV)
-    out = _run(gpu_lib, x, 1)
-    rng = np.random.default_rng(B * 100 + Hkv)
-    n_rows = min(B * 32, 48)
-    flat = rng.choice(B * 32, size=n_rows, replace=False)
-    rows = [(int(i) // 32, int(i) % 32) for i in flat]
-    c = x.to("cpu")
-    ref = oracle.decode_paged_rows(c.q, c.k_cache, c.v_cache, c.page_table, c.context_lens,
-                                   c.scale, rows)
-    got = np.stack([to_f64(out[b, h]) for (b, h) in rows])
-    want = np.stack([ref[r] for r in rows])
-    assert_close(got, want, "bf16", f"config5 B={B} Hkv={Hkv}")
+    ref = _ref(x)
+    assert_close(_run(gpu_lib, x, 1), ref, "bf16", f"config5 B={B} Hkv={Hkv} split")
+    assert_close(_run_bal(gpu_lib, x), ref, "bf16", f"config5 B={B} Hkv={Hkv} balanced")
+    del x
 
 
 # ---------------------------------------------------------------- gather / combine
@@ -231,24 +227,55 @@ def _run_bal(g, x):
     return out
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-D{c[1]}-{c[2]}x{c[3]}")
-def test_balanced_small_shapes(gpu_lib, case):
+def _route_table(route, B, hq, hkv, lens):
+    """Page-table width that sends a balanced call down `route`: "split" keeps the narrowest
+    table (small problems take the split path), "persistent" widens it past the small-problem
+    limit (1,024 (sequence, KV head, page) items, 65,536 for G = 1)."""
+    if route == "split":
+        return None
+    limit = 65536 if hq // hkv == 1 else 1024
+    return max(max((t + 15) // 16 for t in lens), 1, limit // (B * hkv) + 1)
+
+
+def _bal_inputs(g, route, B, hq, hkv, D, lens, dtype, seed, **kw):
+    x = synth.decode_inputs(B, hq, hkv, D, 16, lens, dtype, seed=seed, device=DEV,
+                            max_pages=_route_table(route, B, hq, hkv, lens), **kw)
+    r = g.balanced_route(B, hq, hkv, D, x.page_table.shape[1])
+    assert (r == 0) == (route == "persistent"), f"route {r} for a {route} case"
+    return x
+
+
+# the persistent kernel serves G <= 8 only
+BAL_CASES = [(c, r) for c in SMALL for r in ("split", "persistent")
+             if r == "split" or c[2] // c[3] <= 8]
+
+
+@pytest.mark.parametrize("case,route", BAL_CASES,
+                         ids=lambda c: c if isinstance(c, str) else f"{c[0]}-D{c[1]}-{c[2]}x{c[3]}")
+def test_balanced_small_shapes(gpu_lib, case, route):
     dtype, D, hq, hkv, lens = case
-    print(f"[balanced] small {case}", flush=True)
-    x = synth.decode_inputs(len(lens), hq, hkv, D, 16, lens, dtype,
-                            seed=D + 7 * hq + 13 * hkv + len(lens), device=DEV)
-    assert_close(_run_bal(gpu_lib, x), _ref(x), dtype, f"balanced {case}")
+    print(f"[balanced] small {case} {route}", flush=True)
+    x = _bal_inputs(gpu_lib, route, len(lens), hq, hkv, D, lens, dtype,
+                    seed=D + 7 * hq + 13 * hkv + len(lens))
+    assert_close(_run_bal(gpu_lib, x), _ref(x), dtype, f"balanced {case} {route}")
 
 
-def test_balanced_config1_and_empty_sequences(gpu_lib):
-    print("[balanced] config1 / empty", flush=True)
-    x = synth.config1(device=DEV)
-    assert_close(_run_bal(gpu_lib, x), _ref(x), "f32", "balanced config1")
-    y = synth.decode_inputs(5, 8, 2, 128, 16, [0, 1, 0, 17, 0], "bf16", seed=5, device=DEV)
-    out = _run_bal(gpu_lib, y)
+@pytest.mark.parametrize("route", ["split", "persistent"])
+def test_balanced_config1_and_empty_sequences(gpu_lib, route):
+    print(f"[balanced] config1 / empty {route}", flush=True)
+    # workload 1's inputs, in a page table as wide as the route needs
+    x = synth.config1(device=DEV, max_pages=_route_table(route, 2, 8, 2, [256, 256]))
+    r = gpu_lib.balanced_route(2, 8, 2, 64, x.page_table.shape[1])
+    assert (r == 0) == (route == "persistent")
+    assert_close(_run_bal(gpu_lib, x), _ref(x), "f32", f"balanced config1 {route}")
+    y = _bal_inputs(gpu_lib, route, 5, 8, 2, 128, [0, 1, 0, 17, 0], "bf16", seed=5)
+    out = torch.full_like(y.q, float("nan"))
+    gpu_lib.decode_paged_balanced(y.q, y.k_cache, y.v_cache, y.page_table, y.context_lens,
+                                  scale=y.scale, out=out)
+    _sync()
     for b in (0, 2, 4):
         assert torch.all(out[b] == 0)
-    assert_close(out, _ref(y), "bf16", "balanced empty")
+    assert_close(out, _ref(y), "bf16", f"balanced empty {route}")
 
 
 def test_balanced_config2_parity_determinism_permutation(gpu_lib, cfg2):
@@ -271,9 +298,10 @@ def test_balanced_config2_parity_determinism_permutation(gpu_lib, cfg2):
     assert torch.equal(a, moved)
 
 
-def test_balanced_poison(gpu_lib):
-    print("[balanced] poison", flush=True)
-    x = synth.decode_inputs(3, 32, 8, 128, 16, [37, 300, 16], "bf16", seed=8, device=DEV)
+@pytest.mark.parametrize("route", ["split", "persistent"])
+def test_balanced_poison(gpu_lib, route):
+    print(f"[balanced] poison {route}", flush=True)
+    x = _bal_inputs(gpu_lib, route, 3, 32, 8, 128, [37, 300, 16], "bf16", seed=8)
     clean_k = torch.nan_to_num(x.k_cache, nan=0.0)
     clean_v = torch.nan_to_num(x.v_cache, nan=0.0)
     pt_far = x.page_table.clone()
@@ -292,61 +320,89 @@ def test_balanced_config4(gpu_lib, B):
     assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"balanced config4 B={B}")
 
 
-@pytest.mark.parametrize("Hkv", synth.CONFIG5_KV_HEADS)
-@pytest.mark.parametrize("B", (1, 16, 256))
-def test_balanced_config5(gpu_lib, B, Hkv):
-    print(f"[balanced] config5 B={B} Hkv={Hkv}", flush=True)
-    x = synth.config5(B, Hkv, device=DEV)
-    out = _run_bal(gpu_lib, x)
-    rng = np.random.default_rng(B * 100 + Hkv + 1)
-    n_rows = min(B * 32, 48)
-    flat = rng.choice(B * 32, size=n_rows, replace=False)
-    rows = [(int(i) // 32, int(i) % 32) for i in flat]
-    c = x.to("cpu")
-    ref = oracle.decode_paged_rows(c.q, c.k_cache, c.v_cache, c.page_table, c.context_lens,
-                                   c.scale, rows)
-    got = np.stack([to_f64(out[b, h]) for (b, h) in rows])
-    want = np.stack([ref[r] for r in rows])
-    assert_close(got, want, "bf16", f"balanced config5 B={B} Hkv={Hkv}")
-
-
 @pytest.mark.parametrize("B,hq,hkv,T", [(1, 32, 8, 1024), (1, 32, 32, 1024), (2, 8, 2, 100),
                                          (1, 4, 1, 16), (3, 32, 8, 40)])
 def test_balanced_small_batches_use_fewer_waves(gpu_lib, B, hq, hkv, T):
-    """Batches with fewer than a few pages per resident wave: only N / 4 waves take a share
-    (the others must return at once) and the merge of cut units uses the same partition."""
+    """Persistent kernel on batches with fewer than a few pages per resident wave: only N / 4
+    waves take a share (the others must return at once) and the merge of cut units uses the
+    same partition (the page table is widened so that the balanced entry point does not
+    hand these small problems to the split path)."""
     print(f"[balanced] small batch B={B} {hq}x{hkv} T={T}", flush=True)
-    x = synth.decode_inputs(B, hq, hkv, 128, 16, [T] * B, "bf16", seed=B * 31 + T, device=DEV)
+    x = _bal_inputs(gpu_lib, "persistent", B, hq, hkv, 128, [T] * B, "bf16", seed=B * 31 + T)
     assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"small batch B={B} T={T}")
 
 
-def test_balanced_all_sequences_empty_and_clamped_lengths(gpu_lib):
-    """A batch with no cached token at all (the kernels see N = 0 items) gives zero rows over
-    a NaN-filled output; lengths past what the page-table row addresses are clamped to it."""
-    print("[balanced] all empty / clamped", flush=True)
+@pytest.mark.parametrize("route", ["split", "persistent"])
+def test_balanced_all_sequences_empty_and_clamped_lengths(gpu_lib, route):
+    """A batch with no cached token at all (the persistent kernel sees N = 0 items) gives zero
+    rows over a NaN-filled output; lengths past what the page-table row addresses are clamped
+    to it."""
+    print(f"[balanced] all empty / clamped {route}", flush=True)
     for dtype, hq, hkv in (("bf16", 32, 8), ("f32", 8, 2), ("bf16", 32, 2)):
-        x = synth.decode_inputs(3, hq, hkv, 128, 16, [0, 0, 0], dtype, seed=61, device=DEV)
+        if route == "persistent" and hq // hkv > 8:
+            continue
+        x = _bal_inputs(gpu_lib, route, 3, hq, hkv, 128, [0, 0, 0], dtype, seed=61)
         out = torch.full_like(x.q, float("nan"))
         gpu_lib.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
                                       scale=x.scale, out=out)
         _sync()
         assert torch.all(out == 0), f"all empty {dtype} {hq}x{hkv}"
-    # max_pages = 4: rows 1 and 2 hold 4 live pages (64 tokens), row 0 three (40 tokens);
-    # only rows whose table is full get a length past it
-    x = synth.decode_inputs(3, 32, 8, 128, 16, [40, 64, 64], "bf16", seed=62, device=DEV)
+    # rows 1 and 2 fill their page-table rows (mp pages), row 0 holds 40 tokens; only rows
+    # whose table is full get a length past it
+    mp = 4 if route == "split" else 43  # 3 * 8 * 43 = 1032 items > 1024
+    full = mp * 16
+    x = _bal_inputs(gpu_lib, route, 3, 32, 8, 128, [40, full, full], "bf16", seed=62)
+    assert x.page_table.shape[1] == mp
     ref = _ref(x)
-    big = torch.tensor([40, 10_000, 2**30], dtype=torch.int32, device=DEV)
+    big = torch.tensor([40, full + 10_000, 2**30], dtype=torch.int32, device=DEV)
     out = gpu_lib.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, big,
                                         scale=x.scale)
     _sync()
-    assert_close(out, ref, "bf16", "balanced clamped lengths")
+    assert_close(out, ref, "bf16", f"balanced clamped lengths {route}")
+
+
+@pytest.mark.parametrize("B,hq,hkv,mp,route", [
+    (4, 32, 8, 32, "split"), (5, 20, 5, 41, "persistent"),        # G = 4: 1,024 / 1,025 items
+    (2, 8, 8, 4096, "split"), (1, 1, 1, 65537, "persistent"),     # G = 1: 65,536 / 65,537
+])
+def test_balanced_route_limit_parity(gpu_lib, B, hq, hkv, mp, route):
+    """Both sides of the small-problem limit of the balanced entry point match the oracle."""
+    print(f"[balanced] route limit B={B} {hq}x{hkv} max_pages={mp} {route}", flush=True)
+    lens = [(37 * (b + 3)) % (mp * 16) + 1 for b in range(B)]
+    x = synth.decode_inputs(B, hq, hkv, 128, 16, lens, "bf16", seed=mp + B, device=DEV,
+                            max_pages=mp)
+    assert B * hkv * mp in (1024, 1025, 65536, 65537)
+    assert (gpu_lib.balanced_route(B, hq, hkv, 128, mp) == 0) == (route == "persistent")
+    assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"route limit {route}")
+
+
+def test_balanced_long_context_repeats_are_bitwise_identical(gpu_lib):
+    """Workload 4 at B = 1 (one sequence of 32,768 tokens: each of its 8 units is cut into
+    hundreds of pieces merged in two levels through device-scope counters): 50 calls in a row
+    on one workspace give bit-identical outputs (an ordering fault in the merge would show as
+    a differing or unwritten row)."""
+    print("[balanced] config4 B=1 x50", flush=True)
+    x = synth.config4(1, device=DEV)
+    assert gpu_lib.balanced_route(1, 32, 8, 128, x.page_table.shape[1]) == 0
+    ws = gpu_lib.balanced_workspace(1, 32, 8, 128, DEV)
+    first = None
+    for i in range(50):
+        out = torch.full_like(x.q, float("nan"))
+        gpu_lib.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table, x.context_lens,
+                                      scale=x.scale, out=out, workspace=ws)
+        _sync()
+        if first is None:
+            first = out
+            assert torch.isfinite(first.float()).all()
+        else:
+            assert torch.equal(out, first), f"call {i} differs from the first"
 
 
 def test_balanced_workspace_reused_across_shapes(gpu_lib):
     """One zero-filled workspace serves a run of calls with different head shapes and length
     mixes (units cut into 2 pieces, into hundreds of pieces, empty sequences, the G >= 16 split
-    path in between): every result matches the oracle, rows of empty sequences are written as
-    zeros over a NaN-filled output, and the leading counters are zero again after every call."""
+    path in between): every result matches the oracle and rows of empty sequences are written
+    as zeros over a NaN-filled output (the counters are reused under new epochs)."""
     import gqa_paged_kv_amd as gk
     cases = [
         ("bf16", 32, 8, [37, 300, 16, 0, 1000, 5, 0, 64]),
@@ -371,20 +427,24 @@ def test_balanced_workspace_reused_across_shapes(gpu_lib):
         for b, t in enumerate(lens):
             if t == 0:
                 assert torch.all(out[b] == 0), f"case {i}: empty sequence {b} not zeroed"
-        assert torch.all(ws[:gk.BALANCED_WS_RESERVED] == 0), f"case {i}: counters left non-zero"
 
 
 # ---------------------------------------------------------------- scale sign and magnitude
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.7])
-@pytest.mark.parametrize("path", ["split1", "split3", "balanced", "balanced_g16"])
+@pytest.mark.parametrize("path", ["split1", "split3", "balanced_split", "balanced_persistent",
+                                  "balanced_g16"])
 def test_decode_scale_sign_and_magnitude(gpu_lib, scale, path):
     """The kernels take the row max of raw q.k and apply the scale in the exponent; a negative
     scale (the max becomes the min), a zero scale (uniform weights; dead slots must still get
     weight 0) and a large one must all match the oracle. Ragged lengths leave dead slots."""
     print(f"[decode] scale {scale} {path}", flush=True)
     hq, hkv = (32, 2) if path == "balanced_g16" else (8, 2)
-    x = synth.decode_inputs(3, hq, hkv, 128, 16, [37, 200, 5], "bf16", seed=91, device=DEV)
+    if path.startswith("balanced"):
+        route = "persistent" if path == "balanced_persistent" else "split"
+        x = _bal_inputs(gpu_lib, route, 3, hq, hkv, 128, [37, 200, 5], "bf16", seed=91)
+    else:
+        x = synth.decode_inputs(3, hq, hkv, 128, 16, [37, 200, 5], "bf16", seed=91, device=DEV)
     x.scale = scale
     if path.startswith("split"):
         out = _run(gpu_lib, x, ns=int(path[-1]))

@@ -75,34 +75,29 @@ def cfg3():
     return x, kb, vb
 
 
-def test_config3_prefill_sampled_heads_and_append(gpu_lib, cfg3):
-    print("[prefill] config3", flush=True)
+def test_config3_prefill_whole_output_and_append(gpu_lib, cfg3):
+    """Workload 3 at full size (B=4, S=2048, Hq=32, Hkv=8, the launch the benchmark times):
+    every (b, head) row of the output against the float64 oracle, and the whole append."""
+    print("[prefill] config3 whole output", flush=True)
     x, kb, vb = cfg3
     out = _run(gpu_lib, x)
     _check_append(x, kb, vb)
     c = x.to("cpu")
-    rows = [(b, h) for b in range(4) for h in (b, 8 + 3 * b, 31 - b)]  # every b, spread heads
-    ref = oracle.prefill_causal_rows(c.q, c.k, c.v, c.scale, rows)
-    got = np.stack([to_f64(out[b, :, h]) for (b, h) in rows])
-    want = np.stack([ref[r] for r in rows])
-    assert_close(got, want, "bf16", "config3 sampled heads")
+    ref = oracle.prefill_causal(c.q, c.k, c.v, c.scale)
+    assert_close(out, ref, "bf16", "config3 whole output")
 
 
-def test_prefill_long_sequence_sampled_heads(gpu_lib):
+def test_prefill_long_sequence_whole_output(gpu_lib):
     """S = 8192 (4x the benchmark length: 128 key tiles for the last q-tile, the running max
-    raised many times): two sampled heads against the oracle, and the append of all 8192
-    positions."""
+    raised many times): every head against the oracle, and the append of all 8192 positions."""
     print("[prefill] S=8192", flush=True)
     x = synth.prefill_inputs(1, 8192, 8, 2, 128, 16, seed=8192, device=DEV)
     kb, vb = x.k_cache.cpu(), x.v_cache.cpu()
     out = _run(gpu_lib, x)
     _check_append(x, kb, vb)
     c = x.to("cpu")
-    rows = [(0, 1), (0, 6)]
-    ref = oracle.prefill_causal_rows(c.q, c.k, c.v, c.scale, rows)
-    got = np.stack([to_f64(out[b, :, h]) for (b, h) in rows])
-    want = np.stack([ref[r] for r in rows])
-    assert_close(got, want, "bf16", "prefill S=8192 sampled heads")
+    ref = oracle.prefill_causal(c.q, c.k, c.v, c.scale)
+    assert_close(out, ref, "bf16", "prefill S=8192 whole output")
 
 
 def test_config3_deterministic(gpu_lib, cfg3):
@@ -146,7 +141,7 @@ def test_prefill_more_kv_pairs_than_compute_units(gpu_lib):
 def test_prefill_several_q_tiles_per_workgroup(gpu_lib, B, S, hq, hkv):
     """More q-tiles than workgroups per (b, kv head) pair on a 256-CU device: every
     workgroup processes several q-tiles in a row (G = 8, 4, 2, 1; the last round only partly
-    filled, S not a multiple of the q-tile); sampled heads against the oracle, the whole
+    filled, S not a multiple of the q-tile); the whole output against the oracle, the whole
     append bit for bit."""
     print(f"[prefill] several items B={B} S={S} {hq}x{hkv}", flush=True)
     x = synth.prefill_inputs(B, S, hq, hkv, 128, 16, seed=B * S + hq, device=DEV)
@@ -154,9 +149,5 @@ def test_prefill_several_q_tiles_per_workgroup(gpu_lib, B, S, hq, hkv):
     out = _run(gpu_lib, x)
     _check_append(x, kb, vb)
     c = x.to("cpu")
-    rows = [(0, 0), (B - 1, hq - 1), (B // 2, hq // 2 + 1)]
-    ref = oracle.prefill_causal_rows(c.q, c.k, c.v, c.scale, rows)
-    got = np.stack([to_f64(out[b, :, h]) for (b, h) in rows])
-    want = np.stack([ref[r] for r in rows])
-    assert_close(got, want, "bf16", f"prefill several items B={B} S={S}")
-    assert torch.isfinite(out.float()).all()
+    ref = oracle.prefill_causal(c.q, c.k, c.v, c.scale)
+    assert_close(out, ref, "bf16", f"prefill several items B={B} S={S}")
