@@ -155,14 +155,14 @@ def decode_paged(q, k_cache, v_cache, page_table, context_lens, num_splits: int 
 
 
 # Leading bytes of a balanced-decode workspace that hold counters (zero before first use;
-# every call tags them with a new epoch, so nothing needs clearing between calls).
+# every completed call leaves them zero, every call tags them with a new epoch).
 BALANCED_WS_RESERVED = 98304
 
 
 def balanced_workspace(B: int, Hq: int, Hkv: int, D: int, device):
     """Device scratch for decode_paged_balanced / decode_append / decode_paged_fp8 (uint8
-    tensor, 256-byte aligned, zero-filled: its leading counters must start at zero; calls
-    tag them with increasing epochs, so the tensor can be reused by calls enqueued in order)."""
+    tensor, 256-byte aligned, zero-filled: its leading counters must start at zero; every
+    completed call leaves them zero, so the tensor can be reused by calls enqueued in order)."""
     n = int(load().gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D))
     return torch.zeros(n, dtype=torch.uint8, device=device)
 

@@ -20,7 +20,7 @@
 // whole 128-byte lines. After its last page a wave counts its pieces on per-group /
 // per-unit counters (device-scope atomics, tagged with the call's epoch); the piece that
 // completes a count merges (a group of up to kGroup pieces, then the group partials of a long
-// unit), so no second launch and no cache flush is needed. Each wave keeps pages in
+// unit) and resets the counter, so no second launch and no cache flush is needed. Each wave keeps pages in
 // flight in VGPRs while it computes one; all G <= 8 heads of the group live in the wave,
 // so a K/V row is read once. Rows of sequences with T_b = 0 are zero-filled.
 #include <atomic>
@@ -37,9 +37,10 @@ constexpr int kBalancedMaxWaves = 4096;  // upper bound of the persistent grid (
 // slots of SlotGeom::FLOATS floats (whole 128-byte lines). A counter holds
 // (epoch << kEpochShift) + count: every call takes a new, larger epoch from the host, and a
 // piece first raises the counter to its call's base (atomic max), then counts on it (atomic
-// add), so whatever an earlier call left in a counter (a finished call's full count, or the
-// partial count of a call that never completed) is discarded by the next call. The counters
-// must hold zero (or any earlier epoch's value) before the first call on a workspace.
+// add), so a partial count that an earlier call left behind (a call that never completed) is
+// discarded by the next call. The piece that completes a count resets the counter to zero, so
+// a launch replayed with the same epoch (a captured graph) also starts from zero. The
+// counters must hold zero (or an earlier epoch's value) before the first call on a workspace.
 constexpr int kGroup = 8;  // pieces merged together at the first level
 constexpr int kEpochShift = 16;  // counts stay below 2^16 (at most kBalancedMaxWaves pieces)
 static_assert(GQA_BALANCED_WS_RESERVED == 3 * kBalancedMaxWaves * 8, "counter region");
@@ -536,6 +537,11 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     asm volatile("" ::: "memory");
     return (long)(old + 1 - epoch_base);
   };
+  // The piece that completes a count sets the counter back to zero, which every later call
+  // (a new epoch, or a replay of this same launch with the same epoch) starts from.
+  auto clear = [&](unsigned long long* c) {
+    if (lane == 0) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   auto publish = [&](const Piece& pc) {
     const int w0 = share_owner(N, pc.first, nw);
     const int w1 = share_owner(N, pc.first + pc.np - 1, nw);
@@ -547,6 +553,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     const int ngroups = (npc + kGroup - 1) / kGroup;
     unsigned long long* gc = group_cnt + 2 * gfirst + (g == 0 ? s0 : 0);
     if (count_in(gc) != gsize) return;  // another piece of the group is still running
+    clear(gc);
     auto piece_off = [&](int p) { return slot_off(gfirst + p, (g == 0 && p == 0) ? s0 : 0); };
     if (ngroups == 1) {
       merge_pieces<T, D, G, true>(rs, gsize, piece_off, out + pc.dst, 0u, lane);
@@ -556,6 +563,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     unsigned long long* uc = unit_cnt + w0;
     if (count_in(uc) != ngroups) return;
+    clear(uc);
     auto group_off = [&](int gg) { return slot_off(w0 + gg * kGroup, gg == 0 ? s0 : 0); };
     merge_pieces<T, D, G, true>(rs, ngroups, group_off, out + pc.dst, 0u, lane);
   };

@@ -60,9 +60,9 @@ typedef enum {
 } gqa_status;
 
 /* Bytes at the start of a balanced-decode workspace that hold 64-bit counters. They must be
- * zero before the first call that uses the workspace; every call then tags them with a new
- * epoch, so they need no clearing between calls, and a call that never completed leaves
- * nothing that a later call would count. */
+ * zero before the first call that uses the workspace; every completed call leaves them zero,
+ * and every call tags them with a new epoch, so a call that never completed leaves nothing
+ * that a later call would count. */
 #define GQA_BALANCED_WS_RESERVED 98304
 
 typedef enum {
@@ -122,8 +122,9 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *   workspace        device scratch of at least
  *                    gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D) bytes, 256-byte
  *                    aligned, owned by the caller. Zero it once after allocating it: its
- *                    first GQA_BALANCED_WS_RESERVED bytes are counters, tagged by every
- *                    call with a new epoch (the rest is overwritten). One workspace serves
+ *                    first GQA_BALANCED_WS_RESERVED bytes are counters that every completed
+ *                    call leaves at zero and every call tags with a new epoch (the rest is
+ *                    overwritten). One workspace serves
  *                    every shape whose size it covers. Calls that share a workspace must
  *                    not overlap in time and must be enqueued in order (from one host
  *                    thread at a time).

@@ -401,8 +401,9 @@ def test_balanced_long_context_repeats_are_bitwise_identical(gpu_lib):
 def test_balanced_workspace_reused_across_shapes(gpu_lib):
     """One zero-filled workspace serves a run of calls with different head shapes and length
     mixes (units cut into 2 pieces, into hundreds of pieces, empty sequences, the G >= 16 split
-    path in between): every result matches the oracle and rows of empty sequences are written
-    as zeros over a NaN-filled output (the counters are reused under new epochs)."""
+    path in between): every result matches the oracle, rows of empty sequences are written as
+    zeros over a NaN-filled output, and the leading counters are zero again after every call
+    (so a launch replayed with the same epoch also starts from zero)."""
     import gqa_paged_kv_amd as gk
     cases = [
         ("bf16", 32, 8, [37, 300, 16, 0, 1000, 5, 0, 64]),
@@ -427,6 +428,7 @@ def test_balanced_workspace_reused_across_shapes(gpu_lib):
         for b, t in enumerate(lens):
             if t == 0:
                 assert torch.all(out[b] == 0), f"case {i}: empty sequence {b} not zeroed"
+        assert torch.all(ws[:gk.BALANCED_WS_RESERVED] == 0), f"case {i}: counters left non-zero"
 
 
 # ---------------------------------------------------------------- scale sign and magnitude
