@@ -18,7 +18,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgqa.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_SCRATCH = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
 _FP8_CODE = {"e4m3": FP8_E4M3, "e5m2": FP8_E5M2}
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16}
@@ -28,6 +28,7 @@ _p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "gqa_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _p, _p] + [_i] * 8 + [_f, _i, _p]),
     "gqa_decode_paged_balanced": (_i, [_p] * 7 + [_sz] + [_i] * 7 + [_f, _i, _p]),
+    "gqa_decode_paged_balanced_noalloc": (_i, [_p] * 6 + [_i] * 7 + [_f, _i, _p]),
     "gqa_decode_balanced_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "gqa_decode_append": (_i, [_p] * 9 + [_sz] + [_i] * 7 + [_f, _i, _p]),
     "gqa_decode_paged_fp8": (_i, [_p, _p, _p, _f, _f, _p, _p, _p, _p, _sz] + [_i] * 7 + [_f, _i, _p]),
@@ -199,6 +200,39 @@ def decode_paged_balanced(q, k_cache, v_cache, page_table, context_lens,
                                        D, P, page_table.shape[1], num_pages, scale,
                                        _DTYPE_CODE[q.dtype], _stream(q.device))
     _check(st, "gqa_decode_paged_balanced")
+    return out
+
+
+# Bytes of the static device buffer behind decode_paged_balanced_noalloc.
+NOALLOC_SCRATCH_BYTES = 34701312
+
+
+def decode_paged_balanced_noalloc(q, k_cache, v_cache, page_table, context_lens, out,
+                                  scale: float | None = None):
+    """decode_paged_balanced on the library's static device scratch (no workspace argument;
+    the C entry point allocates nothing). ``out`` [B][Hq][D] must be given; it is returned."""
+    lib = load()
+    _need(q, "q", dim=3)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(out, "out", q.dtype, 3)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, Dk = k_cache.shape
+    if Dk != D or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("shapes do not match q")
+    if page_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("page_table / context_lens batch mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = lib.gqa_decode_paged_balanced_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                               _ptr(page_table), _ptr(context_lens), _ptr(out),
+                                               B, Hq, Hkv, D, P, page_table.shape[1], num_pages,
+                                               scale, _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st, "gqa_decode_paged_balanced_noalloc")
     return out
 
 

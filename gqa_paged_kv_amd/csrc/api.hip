@@ -27,6 +27,7 @@ int launch_decode_balanced_fp8(const void* q, const void* k, const void* v, floa
                                float v_scale, const int32_t* pt, const int32_t* lens, void* out,
                                void* ws, int B, int Hq, int Hkv, int D, int max_pages,
                                float scale, int kv_dtype, hipStream_t s);
+int noalloc_scratch(void** ptr, hipStream_t s);
 int launch_prefill(const void* q, const void* k, const void* v, void* out, void* k_cache,
                    void* v_cache, const int32_t* page_table, int max_pages, int B, int S, int Hq,
                    int Hkv, int D, float scale, hipStream_t s);
@@ -97,18 +98,13 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, num_splits, dtype, s);
 }
 
-int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_cache,
+}  // extern "C"
+
+// The balanced decode on a validated call with `workspace` (workspace_bytes of it usable).
+static int decode_balanced_on(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* page_table, const int32_t* context_lens, void* out,
                               void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                              int D, int P, int max_pages, int num_pages, float scale, int dtype,
-                              void* stream) {
-  int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
-                               nullptr, B, Hq, Hkv, D, P, max_pages, num_pages, 1, scale, dtype);
-  if (st != GQA_OK) return st;
-  if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
-  if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
-  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 0, 0, B, max_pages, P, num_pages, stream);
-  hipStream_t s = (hipStream_t)stream;
+                              int D, int max_pages, float scale, int dtype, hipStream_t s) {
   char* data = (char*)workspace;
   const int ns = gqa_decode_balanced_route(B, Hq, Hkv, D, max_pages, workspace_bytes);
   if (ns == 0)
@@ -120,10 +116,48 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
   // the split partials start past the persistent path's counters
   float* ws_o = (float*)(data + GQA_BALANCED_WS_RESERVED);
   float* ws_lse = ws_o + (size_t)B * Hq * ns * D;
-  st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out, ws_o, ws_lse,
-                                B, Hq, Hkv, D, max_pages, ns, scale, dtype, s);
+  const int st = gqa::launch_decode_paged(q, k_cache, v_cache, page_table, context_lens, out,
+                                          ws_o, ws_lse, B, Hq, Hkv, D, max_pages, ns, scale,
+                                          dtype, s);
   if (st != GQA_OK) return st;
   return gqa::launch_combine(ws_o, ws_lse, out, B, Hq, D, ns, dtype, s);
+}
+
+extern "C" {
+
+int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* context_lens, void* out,
+                              void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                              int D, int P, int max_pages, int num_pages, float scale, int dtype,
+                              void* stream) {
+  int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
+                               nullptr, B, Hq, Hkv, D, P, max_pages, num_pages, 1, scale, dtype);
+  if (st != GQA_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255) != 0) return GQA_ERR_INVALID_ARG;
+  if (workspace_bytes < gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D)) return GQA_ERR_INVALID_ARG;
+  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 0, 0, B, max_pages, P, num_pages, stream);
+  return decode_balanced_on(q, k_cache, v_cache, page_table, context_lens, out, workspace,
+                            workspace_bytes, B, Hq, Hkv, D, max_pages, scale, dtype,
+                            (hipStream_t)stream);
+}
+
+int gqa_decode_paged_balanced_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* page_table, const int32_t* context_lens,
+                                      void* out, int B, int Hq, int Hkv, int D, int P,
+                                      int max_pages, int num_pages, float scale, int dtype,
+                                      void* stream) {
+  int st = gqa_validate_decode(q, k_cache, v_cache, page_table, context_lens, out, nullptr,
+                               nullptr, B, Hq, Hkv, D, P, max_pages, num_pages, 1, scale, dtype);
+  if (st != GQA_OK) return st;
+  if (gqa_decode_balanced_workspace_bytes(B, Hq, Hkv, D) > GQA_NOALLOC_SCRATCH_BYTES)
+    return GQA_ERR_SCRATCH;
+  GQA_DEBUG_CHECK_PAGES(page_table, context_lens, nullptr, 0, 0, B, max_pages, P, num_pages, stream);
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  st = gqa::noalloc_scratch(&ws, s);
+  if (st != GQA_OK) return st;
+  return decode_balanced_on(q, k_cache, v_cache, page_table, context_lens, out, ws,
+                            GQA_NOALLOC_SCRATCH_BYTES, B, Hq, Hkv, D, max_pages, scale, dtype, s);
 }
 
 int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,

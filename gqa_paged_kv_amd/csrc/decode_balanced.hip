@@ -24,6 +24,7 @@
 // flight in VGPRs while it computes one; all G <= 8 heads of the group live in the wave,
 // so a K/V row is read once. Rows of sequences with T_b = 0 are zero-filled.
 #include <atomic>
+#include <mutex>
 
 #include "decode_common.h"
 #include "decode_mfma.h"
@@ -569,6 +570,50 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   };
   if (piece0.valid) publish(piece0);
   if (piece1.valid) publish(piece1);
+}
+
+// ---- static scratch of the allocation-free entry point -----------------------------------
+
+// One balanced-decode workspace per device in a file-scope device array: counters, then the
+// partial slots for the largest supported group (G = 8, D = 128); the split route's partials
+// fit in the slot area for every supported shape. Every call on a device shares it.
+static_assert(GQA_NOALLOC_SCRATCH_BYTES ==
+                  GQA_BALANCED_WS_RESERVED + (size_t)kBalancedMaxWaves * 2 *
+                                                 SlotGeom<8, 128>::FLOATS * sizeof(float),
+              "static scratch size");
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+__global__ void zero_words(unsigned long long* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    p[i] = 0ull;
+}
+
+// Device address of this device's `scratch`, looked up once per device (with the device
+// current) by hipGetSymbolAddress; on that first call the counter region is cleared by a small
+// kernel on `s`. Host code never uses the array's own name, which is a host-side stand-in.
+int noalloc_scratch(void** ptr, hipStream_t s) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_LAUNCH;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+        return GQA_ERR_LAUNCH;
+      hipLaunchKernelGGL(zero_words, dim3(48), dim3(256), 0, s, (unsigned long long*)q,
+                         (int)(GQA_BALANCED_WS_RESERVED / 8));
+      if (hipGetLastError() != hipSuccess) return GQA_ERR_LAUNCH;
+      addr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *ptr = p;
+  return GQA_OK;
 }
 
 // ---- host side --------------------------------------------------------------------------

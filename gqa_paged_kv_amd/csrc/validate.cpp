@@ -49,6 +49,7 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_INVALID_ARG: return "invalid argument";
     case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
     case GQA_ERR_LAUNCH: return "kernel launch failed";
+    case GQA_ERR_SCRATCH: return "problem needs more than the static scratch buffer holds";
     default: return "unknown status";
   }
 }

@@ -56,7 +56,8 @@ typedef enum {
   GQA_OK = 0,
   GQA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0, ... */
   GQA_ERR_UNSUPPORTED = 2, /* valid but not built: D, P, G or dtype outside the supported set */
-  GQA_ERR_LAUNCH = 3       /* the HIP runtime refused the kernel launch */
+  GQA_ERR_LAUNCH = 3,      /* the HIP runtime refused the kernel launch */
+  GQA_ERR_SCRATCH = 4      /* the allocation-free entry point's static buffer is too small */
 } gqa_status;
 
 /* Bytes at the start of a balanced-decode workspace that hold 64-bit counters. They must be
@@ -138,6 +139,29 @@ int gqa_decode_paged_balanced(const void* q, const void* k_cache, const void* v_
                               void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                               int D, int P, int max_pages, int num_pages, float scale, int dtype,
                               void* stream);
+
+/* Bytes of the static device buffer of gqa_decode_paged_balanced_noalloc (33.1 MiB per device:
+ * the counters plus partial slots for 4096 waves of the largest group, G = 8, D = 128). */
+#define GQA_NOALLOC_SCRATCH_BYTES 34701312
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gqa_decode_paged_balanced with the library's own
+ * workspace, a file-scope device array of GQA_NOALLOC_SCRATCH_BYTES bytes that each device
+ * holds until the process ends. Arguments, result and route are those of
+ * gqa_decode_paged_balanced without workspace / workspace_bytes. Nothing is allocated or
+ * freed: the first call on a device looks the buffer's address up (hipGetSymbolAddress) and
+ * enqueues one small kernel on `stream` that clears its counters; every completed call leaves
+ * them zero again. All calls on one device share the buffer, so calls that overlap in time on
+ * one device race (enqueue them in order, from one host thread at a time). Returns
+ * GQA_ERR_SCRATCH, with nothing enqueued, if a shape needs more than the buffer holds (every
+ * supported shape fits: the largest need is GQA_NOALLOC_SCRATCH_BYTES itself).
+ */
+int gqa_decode_paged_balanced_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* page_table, const int32_t* context_lens,
+                                      void* out, int B, int Hq, int Hkv, int D, int P,
+                                      int max_pages, int num_pages, float scale, int dtype,
+                                      void* stream);
 
 /*
  * One decode step with its own token appended (the per-step KV append: page "TensorRT对

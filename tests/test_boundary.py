@@ -51,6 +51,7 @@ def test_status_strings(lib):
     assert "invalid" in g.status_string(1)
     assert "unsupported" in g.status_string(2)
     assert "launch" in g.status_string(3)
+    assert "scratch" in g.status_string(4)
 
 
 def test_workspace_bytes(lib):
