@@ -3,20 +3,26 @@
 
 A step is one pass of the decode path (the balanced decode kernel, which also
 merges the units it cut, ``gqa_decode_paged_balanced``; ``--splits NS`` times the
-split path instead) over
-the paged-decode workload: B=64 sequences, Hq=32, Hkv=8, D=128, page 16, context
-lengths uniform in [512, 4096], bf16, pages scattered by a seeded
-permutation. Inputs are resident in HBM before the timed region. ``value`` is
-algorithmic KV bytes (every live K and V row read once) per second of
+split path instead) over the paged-decode workload: B=64 sequences, Hq=32, Hkv=8,
+D=128, page 16, context lengths uniform in [512, 4096], bf16, pages scattered by a
+seeded permutation. Inputs are resident in HBM before the timed region. ``value``
+is algorithmic KV bytes (every live K and V row read once) per second of
 wall-clock step time; ``roofline.achieved`` uses the GPU time per call from one
-HIP event pair on the launch stream around the same timed region. The same run
-also times decode over an E4M3 pool of the same shape, causal prefill (B=4,
-S=2048, Hq=32, Hkv=8, D=128, bf16, KV append included) and chunked prefill
-(4096 cached + 512 new tokens per sequence), reporting TFLOP/s for the causal
-attention flops, plus the float64 oracle on the host cores as a CPU baseline.
+HIP event pair on the launch stream around the same timed region.
+
+The same run also reports, each call timed alone after a 1 GiB read that evicts
+the L2 caches and the Infinity Cache (median, 10th and 90th percentile): decode
+over an E4M3 pool of the same shape; causal prefill (B=4, S=2048, Hq=32, Hkv=8,
+D=128, bf16, KV append included) and chunked prefill (4096 cached + 512 new
+tokens per sequence) in TFLOP/s of the causal attention flops; the long-context
+decode (B in {1, 4, 8}, T=32768) with the balanced partition and NS in
+{1, 4, 8, 16}; the batch/group sweep (B in {1..256} x Hkv in {1, 8, 32}, T=1024)
+through the balanced entry point; the measured HBM / MFMA ceilings; and the
+float64 oracle on the host cores (decode and prefill) as a CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--splits NS]
-                       [--no-prefill] [--no-cpu-baseline] [--no-fp8] [--sweep]
+                       [--no-prefill] [--no-cpu-baseline] [--no-fp8] [--no-sweeps]
+                       [--sweep] [--prefill-sweep]
 """
 
 from __future__ import annotations
@@ -32,6 +38,7 @@ import torch
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), TFLOP/s
 METRIC = "decode KV GB/s (% HBM peak); prefill TFLOPS (% bf16 MFMA peak)"
 DEFAULT_SPLITS = 0  # balanced partition (gqa_decode_paged_balanced)
 
@@ -84,27 +91,125 @@ def event_times(fn, n, stream, flush=None):
     return ts
 
 
-def cpu_baseline_decode(x_cpu, budget_s=12.0):
-    """The float64 oracle over the decode workload's sequences, repeated until ~budget_s."""
+# ---------------- CPU baseline: the float64 oracle in a pool of single-threaded workers --------
+
+_W = {}  # per-worker state of the oracle pool
+
+
+def _oracle_worker_init(tensors, scale):
+    import torch as _t
+    _t.set_num_threads(1)
+    _W["t"], _W["scale"] = tensors, scale
+
+
+def _oracle_decode_task(b):
     import oracle  # test infrastructure: the float64 CPU oracle, timed as a baseline only
+    q, kc, vc, pt, lens = _W["t"]
+    oracle.decode_paged(q[b:b + 1], kc, vc, pt[b:b + 1], lens[b:b + 1], _W["scale"])
+    return b
+
+
+def _oracle_prefill_task(bh):
+    import oracle  # test infrastructure: the float64 CPU oracle, timed as a baseline only
+    q, k, v = _W["t"]
+    oracle.prefill_causal_rows(q, k, v, _W["scale"], [bh])
+    return bh
+
+
+def host_info():
+    """CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "os_cpu_count": os.cpu_count()}
+
+
+def _oracle_pool(tensors, scale):
+    """A spawn pool of single-threaded workers (BLAS pinned to one thread each) holding the
+    CPU tensors in shared memory; at most 16 workers (one GPU's share of the host)."""
+    import torch.multiprocessing as tmp
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        pool = tmp.get_context("spawn").Pool(n, initializer=_oracle_worker_init,
+                                             initargs=(tensors, scale))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return pool, n
+
+
+def cpu_baseline_decode(x_cpu, budget_s=12.0):
+    """The float64 oracle over the decode workload, one sequence (all 32 heads) per task,
+    whole passes over the batch repeated until ~budget_s of wall time."""
     B = x_cpu.q.shape[0]
-    t0w, t0c = time.perf_counter(), time.process_time()
-    done_bytes = 0
-    n = 0
-    while time.perf_counter() - t0w < budget_s:
-        b = n % B
-        T = int(x_cpu.context_lens[b])
-        oracle.decode_paged(x_cpu.q[b:b + 1], x_cpu.k_cache, x_cpu.v_cache,
-                            x_cpu.page_table[b:b + 1], x_cpu.context_lens[b:b + 1], x_cpu.scale)
-        done_bytes += 2 * T * x_cpu.k_cache.shape[1] * x_cpu.k_cache.shape[3] * 2
-        n += 1
-    wall = time.perf_counter() - t0w
-    cpu = time.process_time() - t0c
-    return dict(value=round(done_bytes / wall / 1e9, 4), unit="GB/s",
-                cores=max(1, round(cpu / wall)), kind="oracle",
-                sample=f"float64 oracle, {n} sequence decodes of the decode workload "
-                       f"(all 32 heads each; {done_bytes / 1e6:.0f} MB of KV) in {wall:.1f} s",
-                host_cores=len(os.sched_getaffinity(0)))
+    tensors = (x_cpu.q, x_cpu.k_cache, x_cpu.v_cache, x_cpu.page_table, x_cpu.context_lens)
+    pool, n = _oracle_pool(tensors, x_cpu.scale)
+    try:
+        pool.map(_oracle_decode_task, range(min(B, n)))  # workers import the oracle first
+        per_seq = [2 * int(x_cpu.context_lens[b]) * x_cpu.k_cache.shape[1] *
+                   x_cpu.k_cache.shape[3] * x_cpu.k_cache.element_size() for b in range(B)]
+        t0 = time.perf_counter()
+        passes = 0
+        while passes == 0 or time.perf_counter() - t0 < budget_s:
+            pool.map(_oracle_decode_task, range(B), chunksize=1)
+            passes += 1
+        wall = time.perf_counter() - t0
+    finally:
+        pool.close()
+        pool.join()
+    done = passes * sum(per_seq)
+    return dict(value=round(done / wall / 1e9, 4), unit="GB/s", cores=n, kind="oracle",
+                sample=f"float64 oracle over the whole decode workload ({B} sequences, all "
+                       f"32 heads; {sum(per_seq) / 1e6:.0f} MB of KV per pass), {passes} passes "
+                       f"in {wall:.1f} s on {n} single-threaded worker processes",
+                **host_info())
+
+
+def cpu_baseline_prefill(p_cpu, budget_s=12.0):
+    """The float64 oracle over the causal prefill workload, one (sequence, query head) per
+    task; GFLOP/s counts the causal attention flops (the GPU's measure), whole passes repeated
+    until ~budget_s."""
+    B, S, hq, d = p_cpu.q.shape
+    pool, n = _oracle_pool((p_cpu.q, p_cpu.k, p_cpu.v), p_cpu.scale)
+    rows = [(b, h) for b in range(B) for h in range(hq)]
+    try:
+        pool.map(_oracle_prefill_task, rows[:n])
+        t0 = time.perf_counter()
+        passes = 0
+        while passes == 0 or time.perf_counter() - t0 < budget_s:
+            pool.map(_oracle_prefill_task, rows, chunksize=1)
+            passes += 1
+        wall = time.perf_counter() - t0
+    finally:
+        pool.close()
+        pool.join()
+    fl = passes * prefill_flops(B, S, hq, d)
+    return dict(value=round(fl / wall / 1e9, 2), unit="GFLOP/s", cores=n, kind="oracle",
+                sample=f"float64 oracle over the whole causal prefill workload ({B}x{hq} "
+                       f"(sequence, head) rows of S={S}), {passes} passes in {wall:.1f} s on "
+                       f"{n} single-threaded worker processes; flops counted as the causal "
+                       f"half (the oracle itself computes the full score matrix)",
+                **host_info())
+
+
+def percentiles(ts):
+    """median, 10th and 90th percentile (ms) of a list of durations."""
+    t = sorted(ts)
+    q = lambda f: t[min(len(t) - 1, max(0, round(f * (len(t) - 1))))]
+    return statistics.median(t), q(0.1), q(0.9)
 
 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
@@ -159,7 +264,12 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="extra lines for the split/batch sweeps")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="leave out the long-context and batch/group legs of the JSON line")
+    ap.add_argument("--flushed-calls", type=int, default=20,
+                    help="calls timed alone after an L2 / Infinity Cache flush, per leg")
+    ap.add_argument("--sweep", action="store_true",
+                    help="extra lines: the batch/group sweep under fixed split counts")
     ap.add_argument("--prefill-sweep", action="store_true",
                     help="extra lines: causal prefill over sequence lengths and group sizes")
     args = ap.parse_args()
@@ -178,6 +288,18 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    # 1 GiB streaming read before each flushed call: evicts the L2s and the Infinity Cache
+    scratch = torch.ones(1024 * 2**20 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
+    flush = lambda: g.bench_stream_read(scratch, sink, 8, 1)
+    NF = args.flushed_calls
+
+    def flushed(fn, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        return percentiles(event_times(fn, NF, stream, flush=flush))
 
     # ---------------- decode workload (inputs resident in HBM) ----------------
     x = synth.config2(device=dev)
@@ -219,13 +341,7 @@ def main():
     achieved = nbytes / (ev_avg * 1e-3) / 1e9
     # per-call durations (events around each call) as a cross-check
     ev_call = statistics.fmean(event_times_queued(step, 100, stream))
-
-    # same launch preceded by a 1 GiB read that evicts L2 and the Infinity Cache
-    scratch = torch.ones(1024 * 2**20 // 4, dtype=torch.float32, device=dev)
-    sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
-    flushed = event_times(step, 30, stream,
-                          flush=lambda: g.bench_stream_read(scratch, sink, 8, 1))
-    flushed_med = statistics.median(flushed)
+    fmed, fp10, fp90 = flushed(step, warm=0)
 
     line = {
         "metric": METRIC,
@@ -261,13 +377,19 @@ def main():
             "event_per_call_us": round(ev_call * 1e3, 2),
         },
         "decode_flushed": {
-            "median_us": round(flushed_med * 1e3, 2),
-            "gbs": round(nbytes / (flushed_med * 1e-3) / 1e9, 1),
-            "frac": round(nbytes / (flushed_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "each launch preceded by a 1 GiB streaming read (L2 + Infinity Cache evicted)",
+            "median_us": round(fmed * 1e3, 2), "p10_us": round(fp10 * 1e3, 2),
+            "p90_us": round(fp90 * 1e3, 2),
+            "gbs": round(nbytes / (fmed * 1e-3) / 1e9, 1),
+            "frac": round(nbytes / (fmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": f"{NF} calls, each after a 1 GiB streaming read (L2 + Infinity Cache evicted)",
         },
     }
-    del scratch
+
+    def leg(med, p10, p90, amount, unit_scale, unit, peak):
+        rate = amount / (med * 1e-3) / unit_scale
+        return {"median_us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2),
+                "p90_us": round(p90 * 1e3, 2), "achieved": round(rate, 1), "unit": unit,
+                "frac": round(rate / peak, 4)}
 
     # ---------------- decode over an 8-bit KV pool (workload 2, E4M3) ----------------
     if not args.no_fp8:
@@ -281,19 +403,13 @@ def main():
                                f8.page_table, f8.context_lens, fmt="e4m3", scale=f8.scale,
                                out=f8out, workspace=f8ws)
 
-        for _ in range(10):
-            f8step()
-        torch.cuda.synchronize()
-        f8med = statistics.median(event_times_queued(f8step, 100, stream))
-        f8gbs = f8bytes / (f8med * 1e-3) / 1e9
+        r = leg(*flushed(f8step), f8bytes, 1e9, "GB/s", HBM_PEAK_GBS)
         line["decode_fp8"] = {
             "workload": "paged GQA decode, workload 2 shape (B=64, Hq=32, Hkv=8, D=128, page 16, "
                         "T~U[512,4096]) with an E4M3 KV pool (per-tensor scales), bf16 q/out",
-            "kv_bytes_per_call": f8bytes,
-            "median_us": round(f8med * 1e3, 2),
-            "gbs": round(f8gbs, 1),
-            "roofline": {"bound": "hbm", "achieved": round(f8gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(f8gbs / HBM_PEAK_GBS, 4),
+            "kv_bytes_per_call": f8bytes, **r,
+            "roofline": {"bound": "hbm", "achieved": r["achieved"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": r["frac"],
                          "traffic": measured_traffic("decode_balanced_fp8e4m3_B64_Hq32_Hkv8"),
                          "kernel": "balanced_kernel<bf16,128,4,fp8e4m3> (one launch)"},
         }
@@ -308,25 +424,20 @@ def main():
             g.prefill_causal(p.q, p.k, p.v, p.k_cache, p.v_cache, p.page_table, scale=p.scale,
                              out=pout)
 
-        for _ in range(5):
-            pstep()
-        torch.cuda.synchronize()
-        pt = event_times_queued(pstep, 30, stream)
-        pmed = statistics.median(pt)
-        B, S, hq, d = p.q.shape
-        fl = prefill_flops(B, S, hq, d)
-        tf = fl / (pmed * 1e-3) / 1e12
+        Bp, S, hq, d = p.q.shape
+        fl = prefill_flops(Bp, S, hq, d)
+        r = leg(*flushed(pstep), fl, 1e12, "TFLOP/s", BF16_PEAK_TFLOPS)
         line["prefill"] = {
             "workload": "causal GQA prefill, B=4, S=2048, Hq=32, Hkv=8, D=128, bf16, "
                         "append to page-16 cache",
-            "median_us": round(pmed * 1e3, 2),
-            "tflops": round(tf, 1),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            **r, "tflops": r["achieved"],
+            "roofline": {"bound": "mfma", "achieved": r["achieved"], "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": r["frac"],
                          "traffic": measured_traffic("prefill_causal_bf16_B4_S2048_Hq32_Hkv8"),
                          "kernel": "prefill_causal_kernel<4> (attention + KV append, one launch)"},
             "flops_per_call": fl,
         }
+        p_cpu = p.to("cpu") if not args.no_cpu_baseline else None
         del p, pout
 
         # chunked prefill over a paged context: 4 sequences with 4096 cached tokens each
@@ -339,34 +450,82 @@ def main():
             g.prefill_paged(c.q, c.k, c.v, c.k_cache, c.v_cache, c.page_table, c.past_lens,
                             c.new_lens, scale=c.scale, out=cout)
 
-        for _ in range(5):
-            cstep()
-        torch.cuda.synchronize()
-        cmed = statistics.median(event_times_queued(cstep, 30, stream))
         cfl = chunked_flops(past, new, 32, 128)
-        ctf = cfl / (cmed * 1e-3) / 1e12
+        r = leg(*flushed(cstep), cfl, 1e12, "TFLOP/s", BF16_PEAK_TFLOPS)
         line["chunked_prefill"] = {
             "workload": "chunked prefill over a paged context, B=4, 4096 cached + 512 new tokens "
                         "per sequence, Hq=32, Hkv=8, D=128, bf16, page 16, permuted pages",
-            "median_us": round(cmed * 1e3, 2),
-            "tflops": round(ctf, 1),
-            "roofline": {"bound": "mfma", "achieved": round(ctf, 1), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ctf / BF16_PEAK_TFLOPS, 4),
+            **r, "tflops": r["achieved"],
+            "roofline": {"bound": "mfma", "achieved": r["achieved"], "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": r["frac"],
                          "traffic": measured_traffic("prefill_paged_bf16_B4_P4096_N512_Hq32_Hkv8"),
                          "kernel": "append_at_kernel + prefill_causal_kernel<4, paged> (one call)"},
             "flops_per_call": cfl,
         }
         del c, cout
 
+    # ---------------- long-context split-K decode and the batch / group sweep ----------------
+    if not args.no_sweeps:
+        lc = []
+        for Bl in synth.CONFIG4_BATCHES:
+            xl = synth.config4(Bl, device=dev)
+            nb = kv_bytes(xl)
+            lout = torch.empty_like(xl.q)
+            bws = g.balanced_workspace(Bl, 32, 8, 128, dev)
+            fn = lambda: g.decode_paged_balanced(xl.q, xl.k_cache, xl.v_cache, xl.page_table,
+                                                 xl.context_lens, scale=xl.scale, out=lout,
+                                                 workspace=bws)
+            lc.append({"B": Bl, "partition": "balanced",
+                       **leg(*flushed(fn), nb, 1e9, "GB/s", HBM_PEAK_GBS)})
+            for nsl in synth.CONFIG4_SPLITS:
+                sws = g.alloc_workspace(Bl, 32, 128, nsl, dev) if nsl > 1 else None
+                fn = lambda: g.decode_paged(xl.q, xl.k_cache, xl.v_cache, xl.page_table,
+                                            xl.context_lens, num_splits=nsl, scale=xl.scale,
+                                            out=lout, workspace=sws)
+                lc.append({"B": Bl, "num_splits": nsl,
+                           **leg(*flushed(fn), nb, 1e9, "GB/s", HBM_PEAK_GBS)})
+            del xl, lout, bws
+        line["long_context"] = {
+            "workload": "long-context decode, T=32768, Hq=32, Hkv=8, D=128, bf16, page 16, "
+                        "64 hot keys x4 per sequence; decode + combine per call",
+            "points": lc}
+        bg = []
+        for hkv in synth.CONFIG5_KV_HEADS:
+            for Bs in synth.CONFIG5_BATCHES:
+                xs = synth.config5(Bs, hkv, device=dev)
+                nb = kv_bytes(xs)
+                sout = torch.empty_like(xs.q)
+                bws = g.balanced_workspace(Bs, 32, hkv, 128, dev)
+                fn = lambda: g.decode_paged_balanced(xs.q, xs.k_cache, xs.v_cache,
+                                                     xs.page_table, xs.context_lens,
+                                                     scale=xs.scale, out=sout, workspace=bws)
+                route = g.balanced_route(Bs, 32, hkv, 128, xs.page_table.shape[1])
+                med, p10, p90 = flushed(fn)
+                pt_ = {"B": Bs, "Hkv": hkv, "G": 32 // hkv,
+                       "route": "persistent" if route == 0 else f"split NS={route}",
+                       **leg(med, p10, p90, nb, 1e9, "GB/s", HBM_PEAK_GBS)}
+                if hkv == 1:  # MQA: 4*D flop per (token, query head) on the vector ALU bound
+                    fl = 4.0 * 128 * int(xs.context_lens.sum()) * 32
+                    pt_["valu_frac"] = round(fl / (med * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)
+                bg.append(pt_)
+                del xs, sout, bws
+        line["batch_group"] = {
+            "workload": "batch/group sweep decode, T=1024, Hq=32, D=128, bf16, page 16, "
+                        "through gqa_decode_paged_balanced (the library's route)",
+            "points": bg}
+
     ceil = ceilings(g, dev, stream)
     line["measured_ceiling"] = dict(ceil, decode_frac_of_read=round(achieved / ceil["stream_read_gbs"], 4))
     for key in ("prefill", "chunked_prefill"):
         if key in line:
             line[key]["frac_of_mfma_ceiling"] = round(line[key]["tflops"] / ceil["mfma_bf16_tflops"], 4)
+    del scratch
 
     # ---------------- CPU baseline: the float64 oracle on the host ----------------
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(x.to("cpu"))
+        if not args.no_prefill:
+            line["cpu_baseline_prefill"] = cpu_baseline_prefill(p_cpu)
 
     print(json.dumps(line), flush=True)
 
@@ -403,10 +562,10 @@ def prefill_sweep(g, synth, dev, stream):
 
 
 def sweep(g, synth, dev, stream):
-    """Extra JSON lines: long-context split sweep and batch/group sweep. Every call is timed
-    alone with HIP events after a 1 GiB streaming read that evicts the L2 and the Infinity
-    Cache (the long-context B=1 pool, 134 MB, would otherwise stay in the 256 MB cache);
-    median and 10th / 90th percentile of 20 calls."""
+    """Extra JSON lines: the batch/group sweep under fixed split counts (split path, NS in
+    {1, 2, 4, 8}) next to the library's route. Every call is timed alone with HIP events after
+    a 1 GiB streaming read that evicts the L2 and the Infinity Cache; median and 10th / 90th
+    percentile of 20 calls."""
     scratch = torch.ones(1024 * 2**20 // 4, dtype=torch.float32, device=dev)
     sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
     flush = lambda: g.bench_stream_read(scratch, sink, 8, 1)
@@ -414,28 +573,11 @@ def sweep(g, synth, dev, stream):
     def timed(f, nb, **fields):
         for _ in range(3):
             f()
-        ts = sorted(event_times(f, 20, stream, flush=flush))
-        t = statistics.median(ts)
-        print(json.dumps({**fields, "us": round(t * 1e3, 2), "p10_us": round(ts[2] * 1e3, 2),
-                          "p90_us": round(ts[17] * 1e3, 2),
-                          "gbs": round(nb / (t * 1e-3) / 1e9, 1)}), flush=True)
+        med, p10, p90 = percentiles(event_times(f, 20, stream, flush=flush))
+        print(json.dumps({**fields, "us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2),
+                          "p90_us": round(p90 * 1e3, 2),
+                          "gbs": round(nb / (med * 1e-3) / 1e9, 1)}), flush=True)
 
-    for B in synth.CONFIG4_BATCHES:
-        x = synth.config4(B, device=dev)
-        nb = kv_bytes(x)
-        bws = g.balanced_workspace(B, 32, 8, 128, dev)
-        out = torch.empty_like(x.q)
-        timed(lambda: g.decode_paged_balanced(x.q, x.k_cache, x.v_cache, x.page_table,
-                                              x.context_lens, scale=x.scale, out=out,
-                                              workspace=bws),
-              nb, sweep="long-context", B=B, T=32768, partition="balanced")
-        for ns in synth.CONFIG4_SPLITS:
-            ws = g.alloc_workspace(B, 32, 128, ns, dev) if ns > 1 else None
-            timed(lambda: g.decode_paged(x.q, x.k_cache, x.v_cache, x.page_table,
-                                         x.context_lens, num_splits=ns, scale=x.scale, out=out,
-                                         workspace=ws),
-                  nb, sweep="long-context", B=B, T=32768, num_splits=ns)
-        del x
     for hkv in synth.CONFIG5_KV_HEADS:
         for B in synth.CONFIG5_BATCHES:
             x = synth.config5(B, hkv, device=dev)
