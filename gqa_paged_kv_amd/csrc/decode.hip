@@ -340,6 +340,307 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_lds_kernel(
   merge_and_store<T, D, G>(st, smem, w, r, qd, b, kvh, split, Hq, num_splits, out, ws_o, ws_lse);
 }
 
+// ------------------------------------------------------------------------------------
+// bf16, G >= 16: the group's heads as the columns of matrix-core products. With 16 or 32
+// query heads per KV head a page is a dense contraction (16 tokens x D dims x G heads), the
+// packing of grouped heads into one matrix dimension that page "解锁GQA性能潜力：从批量大小
+// 敏感性到高效优化实践" (section "核心参数调优：PackGQA与NumSplits的协同舞蹈") describes; on the
+// vector ALU the 32-head case is bound by its dot products, not by HBM.
+//
+// K/V tiles (NP pages of K, then NP pages of V) stream into LDS by global_load_lds_dwordx4
+// through an NST-stage ring (the DMA of the next NST - 1 tiles stays in flight during
+// compute). Wave w takes pages w, w + 4, ... of a tile and, per page and per 16 heads:
+//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16, D / 32 steps; A = K rows (ds_read_b128,
+//                  16-byte chunks XOR-swizzled by row), B = q held in registers;
+//                  lane l = 16 g + n gets tokens 4 g .. 4 g + 3 of head n;
+//   softmax        lane-local per head n (log2 domain, lazily raised reference max);
+//   O^T += V^T P^T v_mfma_f32_16x16x16_bf16, D / 16 dim tiles; A = V^T read transposed
+//                  from the token-major tile (ds_read_b64_tr_b16), B = the lane's own
+//                  weights as bf16 (the score layout is the B layout), so the output rows
+//                  of a head stay in the lanes that own its softmax state.
+// The 4 waves' states are merged through LDS at the end (output, or the split partial).
+// ------------------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from a raw buffer into LDS (buffer_load_dwordx4 ... lds; lane i writes
+// LDS bytes m0 + 16 i .. + 15). Issued from assembly so that the compiler does not track the
+// LDS write: it would otherwise wait for every load in flight before each transpose read of
+// LDS. The kernel orders the write itself (s_waitcnt vmcnt on the issuing wave, then a
+// workgroup barrier) before any wave reads that stage.
+__device__ __forceinline__ void dma16_untracked(u32x4_t rsrc, uint32_t voffset, uint32_t m0) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(m0)
+               : "memory");
+}
+// Raw buffer descriptor over `bytes` bytes at a wave-uniform base.
+__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF),
+                 bytes, 0x00020000u};
+}
+
+template <int D>
+struct MqShape {
+  static constexpr int ROW = D * 2;            // bytes per token row
+  static constexpr int PAGE = kPage * ROW;     // bytes per (page, kv head) block
+  static constexpr int CH = ROW / 16;          // 16-byte chunks per row
+  static constexpr int NP = 4;                 // pages per tile (one per wave)
+  static constexpr int STAGE = 2 * NP * PAGE;  // K pages, then V pages
+  static constexpr int NST = D == 128 ? 4 : 6; // ring depth (128 / 96 KiB)
+  static constexpr int LOADS = STAGE / (16 * kDecodeThreads);
+  static constexpr int NC = D / 32;            // 32-dim steps of the score chain
+  static constexpr int DT = D / 16;            // 16-dim tiles of the output
+  static_assert(STAGE % (16 * kDecodeThreads) == 0 && (NST - 1) * LOADS < 64, "ring");
+  // chunk swizzles: K rows are read 16 rows at one chunk, V rows 4 rows x 32 bytes
+  static __device__ __forceinline__ int k_swz(int r) { return r & (CH - 1); }
+  static __device__ __forceinline__ int v_swz(int r) { return ((r & (CH / 2 - 1)) << 1); }
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void decode_mq_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
+    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ context_lens, bf16_t* __restrict__ out,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv, int max_pages,
+    int num_splits, float scale_log2) {
+  using M = MqShape<D>;
+  constexpr int NP = M::NP, NST = M::NST, NH = G / 16;
+  static_assert(G % 16 == 0, "16 heads per product");
+  constexpr int MERGE = kDecodeWaves * (G * (D + 4) + 2 * G) * 4;
+  constexpr int LDS = NST * M::STAGE > MERGE ? NST * M::STAGE : MERGE;
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  const uint32_t smem0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&smem[0];
+
+  const int split = blockIdx.x % num_splits;
+  const int kvh = blockIdx.x / num_splits;
+  const int b = blockIdx.y;
+  const int w = wave_id();
+  const int lane = lane_id();
+  const int n = lane & 15;   // head column (scores / PV B), token row (K reads)
+  const int g = lane >> 4;   // token group: tokens 4g .. 4g + 3 of a page
+  const SplitRange sr = split_range(context_lens, b, split, num_splits, max_pages);
+  const int ntiles = (sr.lp1 - sr.lp0 + NP - 1) / NP;
+  const int32_t* pt_row = page_table + (size_t)b * max_pages;
+  const size_t page_stride = (size_t)Hkv * M::PAGE;
+  const char* k_base = (const char*)k_cache + (size_t)kvh * M::PAGE;
+  const char* v_base = (const char*)v_cache + (size_t)kvh * M::PAGE;
+  const float sl2 = abs_scale(scale_log2);
+
+  // q of head 16 h + n, dims 32 c + 8 g .. + 7 (the B operand of the score chain); a
+  // negative scale is moved onto q (exact sign flips) and |scale| goes into the exponent.
+  u32x4_t qb[NH][M::NC];
+  {
+    const uint32_t flip = scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const char* src = (const char*)(q + ((size_t)b * Hq + kvh * G + 16 * h + n) * D);
+#pragma unroll
+      for (int c = 0; c < M::NC; ++c) qb[h][c] = *(const u32x4_t*)(src + c * 64 + g * 16) ^ flip;
+    }
+  }
+  float mrun[NH], lrun[NH];
+  f32x4_t acc[NH][M::DT];  // O^T: dims 16 t + 4 g + j of head 16 h + n
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    mrun[h] = -INFINITY;
+    lrun[h] = 0.f;
+#pragma unroll
+    for (int t = 0; t < M::DT; ++t) acc[h][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  int pid_next[NP];
+  auto fetch_pids = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) pid_next[j] = pt_row[min(sr.lp0 + tile * NP + j, sr.lp1 - 1)];
+  };
+  // DMA of one tile: lane i of a wave instruction fills 16 bytes at a fixed LDS position
+  // (row r, chunk c of a page block) and fetches the chunk that belongs there, c ^ swz(r).
+  auto issue_tile = [&](int tile, int stg) {
+    int pid[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) pid[j] = pid_next[j];
+    if (tile + 1 < ntiles) fetch_pids(tile + 1);
+    const uint32_t stage = smem0 + stg * M::STAGE;
+#pragma unroll
+    for (int k = 0; k < M::LOADS; ++k) {
+      const int wave_chunk = k * kDecodeThreads + w * kWave;
+      const int blk = wave_chunk * 16 / M::PAGE;  // K pages 0..NP-1, V pages NP..2NP-1
+      const int pos = (wave_chunk * 16) % M::PAGE + lane * 16;
+      const int r = pos / M::ROW;
+      const int c = (pos % M::ROW) / 16;
+      const int src_c = c ^ (blk < NP ? M::k_swz(r) : M::v_swz(r));
+      const u32x4_t rs = raw_rsrc((blk < NP ? k_base : v_base) +
+                                      (size_t)pid[blk % NP] * page_stride, M::PAGE);
+      dma16_untracked(rs, (uint32_t)(r * M::ROW + src_c * 16),
+                      __builtin_amdgcn_readfirstlane(stage + wave_chunk * 16));
+    }
+  };
+
+  auto page = [&](const char* kpage, const char* vpage, int tok0, bool masked) {
+    // scores S^T = K Q^T for both head halves
+    f32x4_t s[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < M::NC; ++c) {
+      const u32x4_t ka = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
+          kpage + n * M::ROW + (((4 * c + g) ^ M::k_swz(n)) << 4));
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                       __builtin_bit_cast(bf16x8_t, qb[h][c]),
+                                                       s[h], 0, 0, 0);
+    }
+    // V^T operands (transposed reads), issued before the softmax so their latency overlaps it
+    s16x4_t va[M::DT];
+    {
+      const int r = 4 * g + (n >> 2);
+      const char* vrow = vpage + r * M::ROW + 8 * (n & 1);
+#pragma unroll
+      for (int t = 0; t < M::DT; ++t) {
+        const int ch = 2 * t + ((n & 3) >> 1);
+        va[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(uintptr_t)(vrow + ((ch ^ M::v_swz(r)) << 4)));
+      }
+    }
+    float x[NH][4], mx[NH];
+    bool trig = false;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[h][j] = s[h][j] * sl2;
+        if (masked && tok0 + 4 * g + j >= sr.t_end) x[h][j] = -INFINITY;
+      }
+      mx[h] = fmaxf(fmaxf(x[h][0], x[h][1]), fmaxf(x[h][2], x[h][3]));
+      trig |= mx[h] > mrun[h] + kLazyLog2;
+    }
+    // The reference max of a head (one value for the 4 token groups) is raised only when a
+    // score exceeds it by more than 2^kLazyLog2; acc and l are rescaled then.
+    if (__any(trig)) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float Mx = fmaxf(mx[h], __shfl_xor(mx[h], 16));
+        Mx = fmaxf(Mx, __shfl_xor(Mx, 32));
+        const float m_new = fmaxf(mrun[h], Mx);
+        const float m_ref = (m_new > mrun[h] + kLazyLog2) ? m_new : mrun[h];
+        const float alpha = (m_ref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun[h] - m_ref);
+        lrun[h] *= alpha;
+        mrun[h] = m_ref;
+#pragma unroll
+        for (int t = 0; t < M::DT; ++t) acc[h][t] *= alpha;
+      }
+    }
+    if (masked) {  // dead slots (tokens >= t_end) may hold NaN: never multiply them
+#pragma unroll
+      for (int t = 0; t < M::DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + 4 * g + i >= sr.t_end) va[t][i] = 0;
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const float msub = mrun[h] == -INFINITY ? 0.f : mrun[h];
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[h][j] - msub);
+      lrun[h] += (p[0] + p[1]) + (p[2] + p[3]);
+      const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      const s16x4_t pb = __builtin_bit_cast(s16x4_t, pk);
+#pragma unroll
+      for (int t = 0; t < M::DT; ++t)
+        acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[t], pb, acc[h][t], 0, 0, 0);
+    }
+  };
+
+  auto compute_tile = [&](int tile, int stg, bool masked_tile) {
+    const char* stage = smem + stg * M::STAGE;
+#pragma unroll
+    for (int j = w; j < NP; j += kDecodeWaves) {
+      const int lp = sr.lp0 + tile * NP + j;
+      if (lp < sr.lp1)
+        page(stage + j * M::PAGE, stage + (NP + j) * M::PAGE, lp * kPage,
+             masked_tile && lp + 1 == sr.lp1);
+    }
+  };
+
+  if (ntiles > 0) fetch_pids(0);
+  for (int t = 0; t < NST - 1; ++t)
+    if (t < ntiles) issue_tile(t, t);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int stg = tile % NST;
+    const int ahead = tile + NST - 1;
+    if (ahead < ntiles) {
+      issue_tile(ahead, ahead % NST);
+      wait_vmcnt<(NST - 1) * M::LOADS>();
+    } else {
+      const int left = ntiles - 1 - tile;  // tiles still in flight after this one
+      if (NST > 5 && left >= 4) wait_vmcnt<(NST > 5 ? 4 * M::LOADS : 0)>();
+      else if (NST > 4 && left >= 3) wait_vmcnt<(NST > 4 ? 3 * M::LOADS : 0)>();
+      else if (NST > 3 && left >= 2) wait_vmcnt<(NST > 3 ? 2 * M::LOADS : 0)>();
+      else if (NST > 2 && left >= 1) wait_vmcnt<(NST > 2 ? M::LOADS : 0)>();
+      else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    compute_tile(tile, stg, tile + 1 == ntiles);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // ---- merge the 4 waves through LDS: per wave m[h], l[h] (head-uniform after the group
+  // sum) and O^T of all heads; then one thread per (head, dim) ----
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float lt = lrun[h];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    lrun[h] = lt;
+  }
+  __syncthreads();
+  constexpr int DP = D + 4;  // padded row: the 16 heads of a store land in different banks
+  float* acc_lds = (float*)smem;                      // [wave][head][DP]
+  float* m_lds = acc_lds + kDecodeWaves * G * DP;     // [wave][head]
+  float* l_lds = m_lds + kDecodeWaves * G;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int hl = 16 * h + n;
+#pragma unroll
+    for (int t = 0; t < M::DT; ++t)
+      *(f32x4_t*)&acc_lds[(w * G + hl) * DP + 16 * t + 4 * g] = acc[h][t];
+    if (g == 0) {
+      m_lds[w * G + hl] = mrun[h];
+      l_lds[w * G + hl] = lrun[h];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+    const int hl = idx / D, d = idx % D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kDecodeWaves; ++ww) Mx = fmaxf(Mx, m_lds[ww * G + hl]);
+    float L = 0.f, A = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < kDecodeWaves; ++ww) {
+        const float wgt = __builtin_amdgcn_exp2f(m_lds[ww * G + hl] - Mx);
+        L += wgt * l_lds[ww * G + hl];
+        A += wgt * acc_lds[(ww * G + hl) * DP + d];
+      }
+    }
+    const float o = (L > 0.f) ? A / L : 0.f;
+    const int hq = kvh * G + hl;
+    if (ws_o == nullptr) {
+      ((uint16_t*)out)[((size_t)b * Hq + hq) * D + d] = f32_to_bf16(o);
+    } else {
+      const size_t row = ((size_t)b * Hq + hq) * num_splits + split;
+      ws_o[row * D + d] = o;
+      if (d == 0) ws_lse[row] = (L > 0.f) ? (Mx + __builtin_log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 // ---- host-side dispatch over (dtype, D, G) ----------------------------------------------
 
 template <typename T, int D, int G>
@@ -358,6 +659,11 @@ static int launch_decode(const void* q, const void* k, const void* v, const int3
     hipLaunchKernelGGL((decode_regs_kernel<T, D, G>), dim3(groups * ns, B), dim3(kRegsThreads), 0,
                        stream, (const T*)q, (const T*)k, (const T*)v, pt, lens, (T*)out, wo, wl,
                        Hq, Hkv, max_pages, ns, kvw, scale * kLog2e);
+  } else if constexpr (sizeof(T) == 2) {
+    // bf16, G >= 16: heads as matrix-core columns
+    hipLaunchKernelGGL((decode_mq_kernel<D, G>), dim3(Hkv * ns, B), dim3(kDecodeThreads), 0,
+                       stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pt, lens,
+                       (bf16_t*)out, wo, wl, Hq, Hkv, max_pages, ns, scale * kLog2e);
   } else {
     hipLaunchKernelGGL((decode_lds_kernel<T, D, G>), dim3(Hkv * ns, B), dim3(kDecodeThreads), 0,
                        stream, (const T*)q, (const T*)k, (const T*)v, pt, lens, (T*)out, wo, wl,
