@@ -486,12 +486,19 @@ def test_shared_prefix_pages(gpu_lib, path, dtype, hq, hkv):
 
 
 def test_shared_prefix_identical_sequences_give_identical_rows(gpu_lib):
-    """Two sequences with the same page-table row, length and query give bit-identical rows."""
+    """Two sequences with the same page-table row, length and query give bit-identical rows on
+    the split path (its split boundaries are relative to each sequence). The balanced
+    partition cuts each sequence where the global share boundaries fall, so its two rows are
+    summed in different pieces: both must match the oracle."""
     print("[decode] shared prefix identical", flush=True)
     x = synth.decode_inputs(3, 32, 8, 128, 16, [500, 777, 500], "bf16", seed=72, poison=False)
     x.page_table[2] = x.page_table[0]
     x.q[2] = x.q[0]
     x = x.to(DEV)
+    ref = _ref(x)
+    for ns in (1, 4):
+        out = _run(gpu_lib, x, ns)
+        assert torch.equal(out[0], out[2]), f"split path ns={ns}"
+        assert_close(out, ref, "bf16", f"identical beams ns={ns}")
     out = _run_bal(gpu_lib, x)
-    assert torch.equal(out[0], out[2])
-    assert_close(out, _ref(x), "bf16", "identical beams")
+    assert_close(out, ref, "bf16", "identical beams (balanced)")
