@@ -272,6 +272,8 @@ def main():
                     help="extra lines: the batch/group sweep under fixed split counts")
     ap.add_argument("--prefill-sweep", action="store_true",
                     help="extra lines: causal prefill over sequence lengths and group sizes")
+    ap.add_argument("--lib", default=None,
+                    help="load this build of the library instead of gqa_paged_kv_amd/libgqa.so")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -284,7 +286,7 @@ def main():
 
     import gqa_paged_kv_amd as g
     import synth
-    g.load()
+    g.load(args.lib) if args.lib else g.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -359,6 +361,7 @@ def main():
         "config": {
             "workload": "paged GQA decode, B=64, Hq=32, Hkv=8, D=128, page 16, "
                         "T~U[512,4096], bf16, permuted pages",
+            "library": os.path.basename(args.lib) if args.lib else "libgqa.so",
             "partition": "balanced (equal page shares per wave)" if ns == 0 else f"{ns} splits",
             "kv_bytes_per_step": nbytes,
             "total_context_tokens": int(x.context_lens.sum()),
@@ -507,6 +510,9 @@ def main():
                 if hkv == 1:  # MQA: 4*D flop per (token, query head) on the vector ALU bound
                     fl = 4.0 * 128 * int(xs.context_lens.sum()) * 32
                     pt_["valu_frac"] = round(fl / (med * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)
+                    if Bs == 256:
+                        pt_["traffic"] = measured_traffic("decode_mq_bf16_B256_Hq32_Hkv1_T1024")
+                        pt_["kernel"] = "decode_mq_kernel<128,32> (matrix-core scores and PV)"
                 bg.append(pt_)
                 del xs, sout, bws
         line["batch_group"] = {

@@ -1,7 +1,11 @@
 """Build libgqa.so (gfx950) in-tree with hipcc, and libgqa_debug.so: the same kernels with
 the entry points compiled with GQA_DEBUG (page ids checked on the host before every launch).
 
-Usage: python -m gqa_paged_kv_amd.build   (or gqa_paged_kv_amd.build.build())
+Usage: python -m gqa_paged_kv_amd.build            (or gqa_paged_kv_amd.build.build())
+       python -m gqa_paged_kv_amd.build --valu-scores
+           also builds libgqa_valu_scores.so, whose balanced bf16 decode computes the scores
+           on the vector ALU instead of the matrix core (for side-by-side measurements:
+           bench.py --lib gqa_paged_kv_amd/libgqa_valu_scores.so)
 """
 from __future__ import annotations
 
@@ -16,6 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqa.so")
 DEBUG_LIB = os.path.join(HERE, "libgqa_debug.so")
+VALU_SCORES_LIB = os.path.join(HERE, "libgqa_valu_scores.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["api.hip", "decode.hip", "decode_balanced.hip", "aux_kernels.hip", "prefill.hip",
@@ -42,8 +47,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libgqa")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libgqa.so next to this file; returns its path."""
+def build(verbose: bool = False, valu_scores: bool = False) -> str:
+    """Compile every source and link libgqa.so (and libgqa_debug.so; with valu_scores also
+    libgqa_valu_scores.so) next to this file; returns the path of libgqa.so."""
     hipcc = _hipcc()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -63,6 +69,10 @@ def build(verbose: bool = False) -> str:
     dbg_obj = os.path.join(objdir, "api.hip.debug.o")
     cmds.append([hipcc, *HIPCC_FLAGS, "-DGQA_DEBUG", "-c", os.path.join(CSRC, "api.hip"), "-o",
                  dbg_obj])
+    valu_obj = os.path.join(objdir, "decode_balanced.hip.valu.o")
+    if valu_scores:
+        cmds.append([hipcc, *HIPCC_FLAGS, "-DGQA_DECODE_VALU_SCORES=1", "-c",
+                     os.path.join(CSRC, "decode_balanced.hip"), "-o", valu_obj])
     # one compiler process per source, at most as many as the host has cores (and 8)
     jobs = max(1, min(len(cmds), os.cpu_count() or 1, 8))
     with ThreadPoolExecutor(jobs) as pool:
@@ -70,7 +80,11 @@ def build(verbose: bool = False) -> str:
             if r.returncode != 0:
                 raise subprocess.CalledProcessError(r.returncode, r.args)
     api_obj = os.path.join(objdir, "api.hip.o")
-    for lib, lib_objs in ((LIB, objs), (DEBUG_LIB, [dbg_obj if o == api_obj else o for o in objs])):
+    bal_obj = os.path.join(objdir, "decode_balanced.hip.o")
+    libs = [(LIB, objs), (DEBUG_LIB, [dbg_obj if o == api_obj else o for o in objs])]
+    if valu_scores:
+        libs.append((VALU_SCORES_LIB, [valu_obj if o == bal_obj else o for o in objs]))
+    for lib, lib_objs in libs:
         tmp = lib + ".tmp"
         cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp]
         if verbose:
@@ -81,4 +95,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, valu_scores="--valu-scores" in sys.argv))

@@ -31,6 +31,10 @@
 
 namespace gqa {
 
+#ifndef GQA_DECODE_VALU_SCORES
+#define GQA_DECODE_VALU_SCORES 0
+#endif
+
 constexpr int kBalancedMaxWaves = 4096;  // upper bound of the persistent grid (workspace size)
 
 // Workspace: GQA_BALANCED_WS_RESERVED bytes of 64-bit counters (kBalancedMaxWaves per-unit
@@ -368,8 +372,10 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   };
 
   // bf16 queries: scores on the matrix core (WaveStateMq, K in its operand layout);
-  // fp32: the vector path
-  constexpr bool kMq = sizeof(T) == 2;
+  // fp32: the vector path. A library built with GQA_DECODE_VALU_SCORES=1 takes the vector
+  // path for bf16 too (the same result within rounding; kept to measure the two side by
+  // side).
+  constexpr bool kMq = sizeof(T) == 2 && !GQA_DECODE_VALU_SCORES;
   using WS = std::conditional_t<kMq, WaveStateMq<T, D, G, TKV>, WaveState<T, D, G, TKV>>;
   const int qsel = kMq ? lane : qd;  // what init() takes
   // page buffers in VGPRs: NB - 1 pages in flight while one is computed (16-bit caches:
