@@ -291,10 +291,11 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    # 1 GiB streaming read before each flushed call: evicts the L2s and the Infinity Cache
+    # 1 GiB read with ordinary (allocating) loads before each flushed call: evicts the L2s and
+    # the Infinity Cache (a streaming read may leave the latter holding the previous call's data)
     scratch = torch.ones(1024 * 2**20 // 4, dtype=torch.float32, device=dev)
     sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
-    flush = lambda: g.bench_stream_read(scratch, sink, 8, 1)
+    flush = lambda: g.bench_flush_read(scratch, sink)
     NF = args.flushed_calls
 
     def flushed(fn, warm=3):
@@ -384,7 +385,7 @@ def main():
             "p90_us": round(fp90 * 1e3, 2),
             "gbs": round(nbytes / (fmed * 1e-3) / 1e9, 1),
             "frac": round(nbytes / (fmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": f"{NF} calls, each after a 1 GiB streaming read (L2 + Infinity Cache evicted)",
+            "note": f"{NF} calls, each after a 1 GiB read with allocating loads (L2 + Infinity Cache evicted)",
         },
     }
 
@@ -570,11 +571,11 @@ def prefill_sweep(g, synth, dev, stream):
 def sweep(g, synth, dev, stream):
     """Extra JSON lines: the batch/group sweep under fixed split counts (split path, NS in
     {1, 2, 4, 8}) next to the library's route. Every call is timed alone with HIP events after
-    a 1 GiB streaming read that evicts the L2 and the Infinity Cache; median and 10th / 90th
+    a 1 GiB read with allocating loads that evicts the L2 and the Infinity Cache; median and 10th / 90th
     percentile of 20 calls."""
     scratch = torch.ones(1024 * 2**20 // 4, dtype=torch.float32, device=dev)
     sink = torch.empty(4 * 256 * 64, dtype=torch.int32, device=dev)
-    flush = lambda: g.bench_stream_read(scratch, sink, 8, 1)
+    flush = lambda: g.bench_flush_read(scratch, sink)
 
     def timed(f, nb, **fields):
         for _ in range(3):

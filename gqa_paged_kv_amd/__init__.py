@@ -46,6 +46,7 @@ SIGNATURES = {
     "gqa_decode_balanced_route": (_i, [_i, _i, _i, _i, _i, _sz]),
     "gqa_check_page_table": (_i, [_p, _p, _i, _i, _i, _i]),
     "gqa_bench_stream_read": (_i, [_p, _sz, _p, _i, _i, _p]),
+    "gqa_bench_flush_read": (_i, [_p, _sz, _p, _p]),
     "gqa_bench_mfma_bf16": (_i, [_p, _i, _i, _p]),
 }
 
@@ -424,6 +425,14 @@ def bench_stream_read(src, sink, blocks_per_cu: int = 8, unroll: int = 8):
     st = load().gqa_bench_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                       blocks_per_cu, unroll, _stream(src.device))
     _check(st, "gqa_bench_stream_read")
+
+
+def bench_flush_read(src, sink):
+    """Bench-only: read all of ``src`` with ordinary loads (evicts the L2s and the Infinity
+    Cache when ``src`` is several times their size)."""
+    st = load().gqa_bench_flush_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                     _stream(src.device))
+    _check(st, "gqa_bench_flush_read")
 
 
 def bench_mfma_bf16(sink, blocks: int, iters: int):

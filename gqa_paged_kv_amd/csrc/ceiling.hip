@@ -6,7 +6,9 @@
 
 namespace gqa {
 
-template <int U>
+// NT: streaming (non-temporal) loads; otherwise ordinary loads, which allocate in every
+// cache level on the way (the eviction read before a timed call).
+template <int U, bool NT = true>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src,
                                                           size_t n16, uint32_t* __restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * 256;
@@ -15,7 +17,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
   for (; i + (U - 1) * stride < n16; i += U * stride) {
     u32x4_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < U; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
 #pragma unroll
     for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
@@ -70,6 +73,13 @@ int gqa_bench_stream_read(const void* src, size_t bytes, uint32_t* sink, int blo
     case 16: hipLaunchKernelGGL(gqa::stream_read_kernel<16>, dim3(grid), dim3(256), 0, s, p, n16, sink); break;
     default: return GQA_ERR_UNSUPPORTED;
   }
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+int gqa_bench_flush_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0) return GQA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL((gqa::stream_read_kernel<1, false>), dim3(256u * 8u), dim3(256), 0,
+                     (hipStream_t)stream, (const gqa::u32x4_t*)src, bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 

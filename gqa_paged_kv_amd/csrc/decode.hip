@@ -142,8 +142,8 @@ __global__ __launch_bounds__(kRegsThreads) void decode_regs_kernel(
     const size_t off = (size_t)pt_row[lp] * page_stride;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      load_row<T, D>(k_base + off + i * 4 * S::ROW, qd, kb[buf][i]);
-      load_row<T, D>(v_base + off + i * 4 * S::ROW, qd, vb[buf][i]);
+      load_row_nt<T, D>(k_base + off + i * 4 * S::ROW, qd, kb[buf][i]);
+      load_row_nt<T, D>(v_base + off + i * 4 * S::ROW, qd, vb[buf][i]);
     }
   };
   auto run = [&](int buf, int lp) {
@@ -362,13 +362,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_lds_kernel(
 // ------------------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// 16 bytes per lane from a raw buffer into LDS (buffer_load_dwordx4 ... lds; lane i writes
-// LDS bytes m0 + 16 i .. + 15). Issued from assembly so that the compiler does not track the
+// 16 bytes per lane from a raw buffer into LDS (buffer_load_dwordx4 ... lds, with the
+// streaming hint: every K/V row is read once; lane i writes LDS bytes m0 + 16 i .. + 15).
+// Issued from assembly so that the compiler does not track the
 // LDS write: it would otherwise wait for every load in flight before each transpose read of
 // LDS. The kernel orders the write itself (s_waitcnt vmcnt on the issuing wave, then a
 // workgroup barrier) before any wave reads that stage.
 __device__ __forceinline__ void dma16_untracked(u32x4_t rsrc, uint32_t voffset, uint32_t m0) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                :
                : "v"(voffset), "s"(rsrc), "{m0}"(m0)
                : "memory");

@@ -406,8 +406,8 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     for (int i = 0; i < 4; ++i) {
       const bool nr = 4 * i + r == new_row;
       if constexpr (!kMq)
-        load_row<TKV, D>(nr ? (const char*)k_new + new_off : kp + i * 4 * S::ROW, qd, kb[buf][i]);
-      load_row<TKV, D>(nr ? (const char*)v_new + new_off : vp + i * 4 * S::ROW, qd, vb[buf][i]);
+        load_row_nt<TKV, D>(nr ? (const char*)k_new + new_off : kp + i * 4 * S::ROW, qd, kb[buf][i]);
+      load_row_nt<TKV, D>(nr ? (const char*)v_new + new_off : vp + i * 4 * S::ROW, qd, vb[buf][i]);
     }
   };
 

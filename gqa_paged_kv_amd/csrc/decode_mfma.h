@@ -68,7 +68,8 @@ struct WaveStateMq {
   static __device__ __forceinline__ int k_off(int lane, int c) {
     return kFp8 ? c * 32 + (lane >> 4) * 8 : c * 64 + (lane >> 4) * 16;
   }
-  // this lane's words of K row `row` (the row k_row(lane) of a page)
+  // this lane's words of K row `row` (the row k_row(lane) of a page); 16-byte loads carry
+  // the streaming hint (see load_row_nt)
   static __device__ __forceinline__ void load_k(const char* row, int lane,
                                                 uint32_t (&kw)[KROWS][KWORDS]) {
 #pragma unroll
@@ -77,7 +78,7 @@ struct WaveStateMq {
         const u32x2_t v = *(const u32x2_t*)(row + k_off(lane, c));
         kw[c][0] = v[0]; kw[c][1] = v[1];
       } else {
-        const u32x4_t v = *(const u32x4_t*)(row + k_off(lane, c));
+        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(row + k_off(lane, c)));
         kw[c][0] = v[0]; kw[c][1] = v[1]; kw[c][2] = v[2]; kw[c][3] = v[3];
       }
     }

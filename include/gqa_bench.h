@@ -26,6 +26,15 @@ int gqa_bench_stream_read(const void* src, size_t bytes, uint32_t* sink, int blo
                           int unroll, void* stream);
 
 /*
+ * Cache eviction before a timed call: reads `bytes` bytes (a multiple of 16) at `src` with
+ * ordinary 128-bit loads, which allocate in the L2 caches and the Infinity Cache (the
+ * streaming loads of gqa_bench_stream_read may bypass the latter), 8 x 256-thread
+ * workgroups per CU. Pass a buffer several times the Infinity Cache (256 MB); `sink` as in
+ * gqa_bench_stream_read.
+ */
+int gqa_bench_flush_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Back-to-back v_mfma_f32_32x32x16_bf16 on register operands: `iters` MFMAs per wave,
  * 8 waves per workgroup, `blocks` workgroups; `sink` gets one float per wave.
  * Flops = blocks * 8 * iters * 32768.
