@@ -10,7 +10,7 @@
 // its own 4 scores per head and the PV products.
 //
 // Lane l (n = l % 16, g = l / 16):
-//   * K operand: token row k_row(l) = (n / 4) + 4 (n % 4) of the page, dims c*32 + g*8 .. +8
+//   * K operand: token row k_row(l) = (n / 4) + 4 (n % 4) of the page, dims q_dim(l, c) .. +8
 //     of chunk c (the row permutation makes output row 4g + j the token g + 4j);
 //   * Q operand: head p*GQ + n % GQ of pass p, the same dims;
 //   * scores: tokens g + 4j (j < 4) of head p*GQ + n % GQ;
@@ -65,19 +65,32 @@ struct WaveStateMq {
     const int n = lane & 15;
     return (n >> 2) + 4 * (n & 3);
   }
-  static __device__ __forceinline__ int k_off(int lane, int c) {
-    return kFp8 ? c * 32 + (lane >> 4) * 8 : c * 64 + (lane >> 4) * 16;
+  // Dims of score step c taken by lane group g = lane / 16 (8 of them, contiguous): 16-bit
+  // caches: c * 32 + g * 8; 8-bit caches: steps 2m and 2m + 1 share one 16-byte load of dims
+  // m * 64 + g * 16 .. + 16, the first 8 for step 2m, the other 8 for step 2m + 1 (the score
+  // is a sum over all dims, so Q only has to follow the same order).
+  static __device__ __forceinline__ int q_dim(int lane, int c) {
+    return kFp8 ? (c >> 1) * 64 + (lane >> 4) * 16 + (c & 1) * 8 : c * 32 + (lane >> 4) * 8;
   }
-  // this lane's words of K row `row` (the row k_row(lane) of a page); 16-byte loads carry
+  // byte offset in a K row of 16-byte load c (8-bit: NC / 2 loads, 16-bit: NC)
+  static __device__ __forceinline__ int k_off(int lane, int c) {
+    return kFp8 ? c * 64 + (lane >> 4) * 16 : c * 64 + (lane >> 4) * 16;
+  }
+  static_assert(!kFp8 || NC % 2 == 0, "8-bit K rows are read 64 dims at a time");
+  // this lane's words of K row `row` (the row k_row(lane) of a page), by 16-byte loads with
   // the streaming hint (see load_row_nt)
   static __device__ __forceinline__ void load_k(const char* row, int lane,
                                                 uint32_t (&kw)[KROWS][KWORDS]) {
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if constexpr (kFp8) {
-        const u32x2_t v = *(const u32x2_t*)(row + k_off(lane, c));
-        kw[c][0] = v[0]; kw[c][1] = v[1];
-      } else {
+      for (int m = 0; m < NC / 2; ++m) {
+        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(row + k_off(lane, m)));
+        kw[2 * m][0] = v[0]; kw[2 * m][1] = v[1];
+        kw[2 * m + 1][0] = v[2]; kw[2 * m + 1][1] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
         const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(row + k_off(lane, c)));
         kw[c][0] = v[0]; kw[c][1] = v[1]; kw[c][2] = v[2]; kw[c][3] = v[3];
       }
@@ -85,13 +98,15 @@ struct WaveStateMq {
   }
   static __device__ __forceinline__ void store_k(char* row, int lane,
                                                  const uint32_t (&kw)[KROWS][KWORDS]) {
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if constexpr (kFp8) {
-        *(u32x2_t*)(row + k_off(lane, c)) = u32x2_t{kw[c][0], kw[c][1]};
-      } else {
+      for (int m = 0; m < NC / 2; ++m)
+        *(u32x4_t*)(row + k_off(lane, m)) =
+            u32x4_t{kw[2 * m][0], kw[2 * m][1], kw[2 * m + 1][0], kw[2 * m + 1][1]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
         *(u32x4_t*)(row + k_off(lane, c)) = u32x4_t{kw[c][0], kw[c][1], kw[c][2], kw[c][3]};
-      }
     }
   }
 
@@ -105,7 +120,7 @@ struct WaveStateMq {
       const char* src = (const char*)(q_head0 + (size_t)(p * GQ + n % GQ) * D);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        u32x4_t v = *(const u32x4_t*)(src + c * 64 + (lane >> 4) * 16);
+        u32x4_t v = *(const u32x4_t*)(src + q_dim(lane, c) * 2);
         qb[p][c] = v ^ flip;
       }
     }
