@@ -177,13 +177,64 @@ __device__ __forceinline__ void store_piece(__amdgpu_buffer_rsrc_t rs, uint32_t 
 // Merge `count` pieces (slot byte offsets off_of(p)) with the log-sum-exp rule. TO_OUT: write
 // the G output rows at dst_row (bf16 / fp32); otherwise write a merged partial (same slot
 // layout) at byte dst_off. Lane p holds piece p's LSEs; the pieces' data are read KB at a time.
-template <typename T, int D, int G, bool TO_OUT, typename OffFn>
-__device__ __forceinline__ void merge_pieces(__amdgpu_buffer_rsrc_t rs, int count, OffFn off_of,
-                                             T* __restrict__ dst_row, uint32_t dst_off,
-                                             int lane) {
+// The first loads of a merge: lane p < min(count, 64) gets piece p's LSEs, every lane its
+// part of the data of pieces 0 .. KB - 1 (the last piece repeated past count). Issued ahead of
+// the merge itself when two merges run back to back, so that their round trips overlap.
+template <int G, int D>
+struct MergeFirst {
+  static constexpr int KB = 8;
+  float lse[G];
+  f32x4_t x[KB][SlotGeom<G, D>::NI];
+  // Uses every loaded value in an empty asm statement: the loads issued so far stay ahead of
+  // this point and are waited for here, together (the scheduler would otherwise move some of
+  // them behind the first wait and pay a second round trip).
+  __device__ __forceinline__ void ready() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) asm volatile("" : "+v"(lse[h]));
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < SlotGeom<G, D>::NI; ++i) asm volatile("" : "+v"(x[kb][i]));
+  }
+};
+template <int D, int G, typename OffFn>
+__device__ __forceinline__ void merge_batch(__amdgpu_buffer_rsrc_t rs, int n_c, int p0,
+                                            OffFn off_of, int lane, MergeFirst<G, D>& mf) {
+  using SG = SlotGeom<G, D>;
+  const int r = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < MergeFirst<G, D>::KB; ++kb) {
+    const uint32_t po = off_of(min(p0 + kb, n_c - 1));
+#pragma unroll
+    for (int i = 0; i < SG::NI; ++i)
+      mf.x[kb][i] = 4 * i + r < SG::NK ? load_sc1(rs, po + (uint32_t)(i * kWave + lane) * 16)
+                                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+template <int D, int G, typename OffFn>
+__device__ __forceinline__ void merge_first(__amdgpu_buffer_rsrc_t rs, int count, OffFn off_of,
+                                            int lane, MergeFirst<G, D>& mf) {
   using SG = SlotGeom<G, D>;
   constexpr int NL = (G + 3) / 4;
-  constexpr int KB = 8;
+  const int n_c = min(kWave, count);
+  const uint32_t lo = off_of(lane < n_c ? lane : 0) + SG::DATA * 4;
+#pragma unroll
+  for (int q4 = 0; q4 < NL; ++q4) {
+    const f32x4_t x = load_sc1(rs, lo + 16 * q4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      if (4 * q4 + kk < G) mf.lse[4 * q4 + kk] = x[kk];
+  }
+  merge_batch<D, G>(rs, n_c, 0, off_of, lane, mf);
+}
+
+template <typename T, int D, int G, bool TO_OUT, bool FIRST = false, typename OffFn>
+__device__ __forceinline__ void merge_pieces(__amdgpu_buffer_rsrc_t rs, int count, OffFn off_of,
+                                             T* __restrict__ dst_row, uint32_t dst_off,
+                                             int lane, const MergeFirst<G, D>* first = nullptr) {
+  using SG = SlotGeom<G, D>;
+  constexpr int NL = (G + 3) / 4;
+  constexpr int KB = MergeFirst<G, D>::KB;
   const int r = lane >> 4;
   const int qd = lane & 15;
   float m_run[G], den[G];
@@ -208,30 +259,22 @@ __device__ __forceinline__ void merge_pieces(__amdgpu_buffer_rsrc_t rs, int coun
   for (int c0 = 0; c0 < count; c0 += kWave) {
     const int n_c = min(kWave, count - c0);
     const bool live = lane < n_c;
-    float lse[G];
-    {
-      const uint32_t lo = off_of(c0 + (live ? lane : 0)) + SG::DATA * 4;
-#pragma unroll
-      for (int q4 = 0; q4 < NL; ++q4) {
-        const f32x4_t x = load_sc1(rs, lo + 16 * q4);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          if (4 * q4 + kk < G) lse[4 * q4 + kk] = x[kk];
-      }
+    // LSEs and the first batch of pieces' data (issued together: the data does not depend
+    // on the LSEs), loaded here or by the caller ahead of time
+    auto off_c = [&](int p) { return off_of(c0 + p); };
+    MergeFirst<G, D> mf;
+    if (FIRST && c0 == 0) {
+      mf = *first;
+    } else {
+      merge_first<D, G>(rs, count - c0, off_c, lane, mf);
+      mf.ready();
     }
-    // the first batch of pieces' data, issued with the LSE loads (it does not depend on them)
-    f32x4_t x[KB][SG::NI];
+    const float (&lse)[G] = mf.lse;
+    f32x4_t (&x)[KB][SG::NI] = mf.x;
     auto load_batch = [&](int p0) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint32_t po = off_of(c0 + min(p0 + kb, n_c - 1));
-#pragma unroll
-        for (int i = 0; i < SG::NI; ++i)
-          x[kb][i] = 4 * i + r < SG::NK ? load_sc1(rs, po + (uint32_t)(i * kWave + lane) * 16)
-                                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      merge_batch<D, G>(rs, n_c, p0, off_c, lane, mf);
+      mf.ready();
     };
-    load_batch(0);
     float w[G], resc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -247,17 +290,19 @@ __device__ __forceinline__ void merge_pieces(__amdgpu_buffer_rsrc_t rs, int coun
     }
 #pragma unroll
     for (int i = 0; i < SG::NI; ++i) num[i] *= lane_head_value(resc, i);
+    // Every piece of the batch is accumulated, also those past n_c: their weight (lane
+    // p0 + kb >= n_c) is 0 and their data is piece n_c - 1's, so they add 0. Without a branch
+    // per piece the compiler keeps every load of the batch ahead of the first wait (one round
+    // trip per batch). p0 + kb <= 63, since n_c <= 64 and p0 < n_c is a multiple of KB.
     for (int p0 = 0;;) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        if (p0 + kb < n_c) {
-          float wu[G];
+        float wu[G];
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-            wu[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[h]), p0 + kb));
+        for (int h = 0; h < G; ++h)
+          wu[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[h]), p0 + kb));
 #pragma unroll
-          for (int i = 0; i < SG::NI; ++i) num[i] += lane_head_value(wu, i) * x[kb][i];
-        }
+        for (int i = 0; i < SG::NI; ++i) num[i] += lane_head_value(wu, i) * x[kb][i];
       }
       p0 += KB;
       if (p0 >= n_c) break;
@@ -300,6 +345,11 @@ __device__ __forceinline__ void merge_pieces(__amdgpu_buffer_rsrc_t rs, int coun
     }
   }
 }
+
+// Shape of the Q staging copy where there is none (vector path).
+struct NoQStage {
+  static constexpr int NPASS = 1, NC = 1;
+};
 
 // T: q / out element type; TKV: cache element type (T, or an 8-bit float whose per-tensor
 // scales are folded in: k_scale into scale_log2, v_scale into out_scale).
@@ -414,6 +464,13 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   WS st;
   long seg_start = lo;  // first item of the current segment
   st.init(q + ((size_t)b * Hq + kvh * G) * D, qsel, scale_log2 < 0.f);
+  // Matrix-core path: the Q words of the unit the load cursor entered last, fetched when it
+  // enters it (NB - 1 items ahead of the compute cursor), so that opening a segment does not
+  // wait on a Q load issued behind the pages in flight. qn_unit: that unit (b * Hkv + kv
+  // head), or -1.
+  using QS = std::conditional_t<kMq, WS, NoQStage>;
+  u32x4_t qn[QS::NPASS][QS::NC];
+  long qn_unit = -1;
   int T_b = seq_len(context_lens, b, max_pages, append);
 
   auto store_row = [&](T* dst, int hw, float inv) {
@@ -496,7 +553,15 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
     advance(b, kvh, pg, np);
     if (unit_end && i + 1 < hi) {
       seg_start = i + 1;
-      st.init(q + ((size_t)b * Hq + kvh * G) * D, qsel, scale_log2 < 0.f);
+      if constexpr (kMq) {
+        if (qn_unit == (long)b * Hkv + kvh) {
+          st.init_from(qn);
+        } else {
+          st.init(q + ((size_t)b * Hq + kvh * G) * D, qsel, scale_log2 < 0.f);
+        }
+      } else {
+        st.init(q + ((size_t)b * Hq + kvh * G) * D, qsel, scale_log2 < 0.f);
+      }
       T_b = seq_len(context_lens, b, max_pages, append);
     }
   };
@@ -506,16 +571,25 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   // an L2 hit) so that the loads in flight are the same on every path and the wait before
   // each page is exactly "all but the NB - 2 newest pages".
   int lb = b, lkv = kvh, lpg = pg, lnp = np;
+  auto advance_load = [&]() {
+    advance(lb, lkv, lpg, lnp);
+    if constexpr (kMq) {
+      if (lpg == 0) {  // the load cursor entered a new unit
+        WS::fetch_q(q + ((size_t)lb * Hq + lkv * G) * D, lane, scale_log2 < 0.f, qn);
+        qn_unit = (long)lb * Hkv + lkv;
+      }
+    }
+  };
   load_page(0, lb, lkv, lpg);
 #pragma unroll
   for (int k = 1; k < NB - 1; ++k) {
-    if (lo + k < hi) advance(lb, lkv, lpg, lnp);
+    if (lo + k < hi) advance_load();
     load_page(k, lb, lkv, lpg);
   }
   for (long i = lo; i < hi; i += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      if (i + k + NB - 1 < hi) advance(lb, lkv, lpg, lnp);
+      if (i + k + NB - 1 < hi) advance_load();
       load_page((k + NB - 1) % NB, lb, lkv, lpg);
       consume(k, i + k);
       if (i + k + 1 >= hi) break;
@@ -549,33 +623,83 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   auto clear = [&](unsigned long long* c) {
     if (lane == 0) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  auto publish = [&](const Piece& pc) {
-    const int w0 = share_owner(N, pc.first, nw);
+  // The group counter of a piece and the shape of its unit's merge.
+  struct Plan {
+    int w0, s0, g, gfirst, gsize, ngroups;
+    unsigned long long* gc;
+  };
+  auto plan_of = [&](const Piece& pc) {
+    Plan pl;
+    pl.w0 = share_owner(N, pc.first, nw);
     const int w1 = share_owner(N, pc.first + pc.np - 1, nw);
-    const int npc = w1 - w0 + 1;                                   // pieces of the unit
-    const int s0 = share_lo(N, w0, nw) == pc.first ? 0 : 1;        // slot of piece 0
-    const int g = (gw - w0) / kGroup;
-    const int gfirst = w0 + g * kGroup;
-    const int gsize = min(kGroup, npc - g * kGroup);
-    const int ngroups = (npc + kGroup - 1) / kGroup;
-    unsigned long long* gc = group_cnt + 2 * gfirst + (g == 0 ? s0 : 0);
-    if (count_in(gc) != gsize) return;  // another piece of the group is still running
-    clear(gc);
-    auto piece_off = [&](int p) { return slot_off(gfirst + p, (g == 0 && p == 0) ? s0 : 0); };
-    if (ngroups == 1) {
-      merge_pieces<T, D, G, true>(rs, gsize, piece_off, out + pc.dst, 0u, lane);
+    const int npc = w1 - pl.w0 + 1;                                   // pieces of the unit
+    pl.s0 = share_lo(N, pl.w0, nw) == pc.first ? 0 : 1;               // slot of piece 0
+    pl.g = (gw - pl.w0) / kGroup;
+    pl.gfirst = pl.w0 + pl.g * kGroup;
+    pl.gsize = min(kGroup, npc - pl.g * kGroup);
+    pl.ngroups = (npc + kGroup - 1) / kGroup;
+    pl.gc = group_cnt + 2 * pl.gfirst + (pl.g == 0 ? pl.s0 : 0);
+    return pl;
+  };
+  auto piece_off_of = [&](const Plan& pl) {
+    return [=](int p) { return slot_off(pl.gfirst + p, (pl.g == 0 && p == 0) ? pl.s0 : 0); };
+  };
+  // The rest of a piece's publication once it has completed its group's count.
+  // (A counter is reset after the merge it released: the reset is a write-through store, and
+  // a store issued before the merge's loads would have its acknowledgement waited for first.)
+  auto complete = [&](const Piece& pc, const Plan& pl) {
+    const auto piece_off = piece_off_of(pl);
+    if (pl.ngroups == 1) {
+      merge_pieces<T, D, G, true>(rs, pl.gsize, piece_off, out + pc.dst, 0u, lane);
+      clear(pl.gc);
       return;
     }
-    merge_pieces<T, D, G, false>(rs, gsize, piece_off, out, piece_off(0), lane);
+    merge_pieces<T, D, G, false>(rs, pl.gsize, piece_off, out, piece_off(0), lane);
+    clear(pl.gc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    unsigned long long* uc = unit_cnt + w0;
-    if (count_in(uc) != ngroups) return;
+    unsigned long long* uc = unit_cnt + pl.w0;
+    if (count_in(uc) != pl.ngroups) return;
+    auto group_off = [&](int gg) { return slot_off(pl.w0 + gg * kGroup, gg == 0 ? pl.s0 : 0); };
+    merge_pieces<T, D, G, true>(rs, pl.ngroups, group_off, out + pc.dst, 0u, lane);
     clear(uc);
-    auto group_off = [&](int gg) { return slot_off(w0 + gg * kGroup, gg == 0 ? s0 : 0); };
-    merge_pieces<T, D, G, true>(rs, ngroups, group_off, out + pc.dst, 0u, lane);
   };
-  if (piece0.valid) publish(piece0);
-  if (piece1.valid) publish(piece1);
+  // Both pieces are counted before either is merged, so that the two counters' round trips
+  // overlap; when this wave completes both units (each a single group of pieces), the first
+  // loads of the two merges are issued together as well.
+  const Plan p0 = piece0.valid ? plan_of(piece0) : Plan{};
+  const Plan p1 = piece1.valid ? plan_of(piece1) : Plan{};
+  unsigned long long old0 = 0, old1 = 0;
+  if (lane == 0) {
+    if (piece0.valid) {
+      __hip_atomic_fetch_max(p0.gc, epoch_base, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old0 = __hip_atomic_fetch_add(p0.gc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (piece1.valid) {
+      __hip_atomic_fetch_max(p1.gc, epoch_base, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old1 = __hip_atomic_fetch_add(p1.gc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const bool done0 = piece0.valid && uniform((long)old0) + 1 - (long)epoch_base == p0.gsize;
+  const bool done1 = piece1.valid && uniform((long)old1) + 1 - (long)epoch_base == p1.gsize;
+  asm volatile("" ::: "memory");
+  if constexpr (G <= 4) {
+    if (done0 && done1 && p0.ngroups == 1 && p1.ngroups == 1) {
+      const auto off0 = piece_off_of(p0);
+      const auto off1 = piece_off_of(p1);
+      MergeFirst<G, D> f0, f1;
+      merge_first<D, G>(rs, p0.gsize, off0, lane, f0);
+      merge_first<D, G>(rs, p1.gsize, off1, lane, f1);
+      f0.ready();
+      f1.ready();
+      merge_pieces<T, D, G, true, true>(rs, p0.gsize, off0, out + piece0.dst, 0u, lane, &f0);
+      merge_pieces<T, D, G, true, true>(rs, p1.gsize, off1, out + piece1.dst, 0u, lane, &f1);
+      clear(p0.gc);
+      clear(p1.gc);
+      return;
+    }
+  }
+  if (done0) complete(piece0, p0);
+  if (done1) complete(piece1, p1);
 }
 
 // ---- static scratch of the allocation-free entry point -----------------------------------

@@ -113,6 +113,13 @@ struct WaveStateMq {
   // q_head0: the group's first query head. neg: the caller's scale is negative; q is
   // negated here (exact) and the kernel runs with |scale|.
   __device__ __forceinline__ void init(const T* q_head0, int lane, bool neg) {
+    fetch_q(q_head0, lane, neg, qb);
+    reset();
+  }
+  // This lane's Q operand words of a group into `dst` (qb itself, or a staging copy for a
+  // unit that starts later).
+  static __device__ __forceinline__ void fetch_q(const T* q_head0, int lane, bool neg,
+                                                 u32x4_t (&dst)[NPASS][NC]) {
     const uint32_t flip = neg ? 0x80008000u : 0u;
     const int n = lane & 15;
 #pragma unroll
@@ -121,9 +128,16 @@ struct WaveStateMq {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         u32x4_t v = *(const u32x4_t*)(src + q_dim(lane, c) * 2);
-        qb[p][c] = v ^ flip;
+        dst[p][c] = v ^ flip;
       }
     }
+  }
+  // init() from Q words fetched earlier by fetch_q.
+  __device__ __forceinline__ void init_from(const u32x4_t (&src)[NPASS][NC]) {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qb[p][c] = src[p][c];
     reset();
   }
 
