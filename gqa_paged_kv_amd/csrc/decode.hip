@@ -523,8 +523,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mq_kernel(
     if (__any(trig)) {
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        float Mx = fmaxf(mx[h], __shfl_xor(mx[h], 16));
-        Mx = fmaxf(Mx, __shfl_xor(Mx, 32));
+        const float Mx = rows4_max(mx[h]);
         const float m_new = fmaxf(mrun[h], Mx);
         const float m_ref = (m_new > mrun[h] + kLazyLog2) ? m_new : mrun[h];
         const float alpha = (m_ref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun[h] - m_ref);
@@ -595,8 +594,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mq_kernel(
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     float lt = lrun[h];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = rows4_sum(lt);
     lrun[h] = lt;
   }
   __syncthreads();

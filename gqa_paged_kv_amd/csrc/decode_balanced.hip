@@ -278,13 +278,11 @@ __device__ __forceinline__ void merge_pieces(__amdgpu_buffer_rsrc_t rs, int coun
     float w[G], resc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float M = live ? lse[h] : -INFINITY;
-      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      float M = wave_max_f32(live ? lse[h] : -INFINITY);
       M = fmaxf(M, m_run[h]);
       resc[h] = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[h] - M) * kLog2e);
       w[h] = live ? __builtin_amdgcn_exp2f((lse[h] - M) * kLog2e) : 0.f;
-      float ws = w[h];
-      for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+      const float ws = wave_sum_f32(w[h]);
       den[h] = den[h] * resc[h] + ws;
       m_run[h] = M;
     }

@@ -157,19 +157,11 @@ struct WaveState {
   __device__ __forceinline__ void merge_rows() {
 #pragma unroll
     for (int hw = 0; hw < HW; ++hw) {
-      float M = fmaxf(m[hw], __shfl_xor(m[hw], 16));
-      M = fmaxf(M, __shfl_xor(M, 32));
+      const float M = rows4_max(m[hw]);
       const float wgt = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[hw] - M);
-      float lw = l[hw] * wgt;
-      lw += __shfl_xor(lw, 16);
-      lw += __shfl_xor(lw, 32);
+      const float lw = rows4_sum(l[hw] * wgt);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float a = acc[hw][e] * wgt;
-        a += __shfl_xor(a, 16);
-        a += __shfl_xor(a, 32);
-        acc[hw][e] = a;
-      }
+      for (int e = 0; e < E; ++e) acc[hw][e] = rows4_sum(acc[hw][e] * wgt);
       m[hw] = M;
       l[hw] = lw;
     }

@@ -159,10 +159,7 @@ struct WaveStateMq {
     float lt[NPASS];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      float x = lrun[p];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      lt[p] = x;
+      lt[p] = rows4_sum(lrun[p]);
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -170,10 +167,7 @@ struct WaveStateMq {
       l[h] = quad_bcast(lt[h / GQ], h % GQ);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        float a = acc[h][e];
-        a += __shfl_xor(a, 16);
-        a += __shfl_xor(a, 32);
-        acc[h][e] = a;
+        acc[h][e] = rows4_sum(acc[h][e]);
       }
     }
   }
@@ -221,11 +215,14 @@ struct WaveStateMq {
       float alpha[NPASS];
 #pragma unroll
       for (int p = 0; p < NPASS; ++p) {
+        // over the lanes of this head: every GQ-th lane of a row (row rotations by
+        // GQ, 2 GQ, ... keep the lane's class mod GQ), then the four rows
         float M = mx[p];
-#pragma unroll
-        for (int o = GQ; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-        M = fmaxf(M, __shfl_xor(M, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
+        if constexpr (GQ == 1) M = fmaxf(M, row_ror<1>(M));
+        if constexpr (GQ <= 2) M = fmaxf(M, row_ror<2>(M));
+        M = fmaxf(M, row_ror<4>(M));
+        M = fmaxf(M, row_ror<8>(M));
+        M = rows4_max(M);
         const float m_new = fmaxf(mrun[p], M);
         const float m_ref = (m_new > mrun[p] + kLazyLog2) ? m_new : mrun[p];
         alpha[p] = (m_ref == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun[p] - m_ref);

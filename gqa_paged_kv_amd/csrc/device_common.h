@@ -106,6 +106,48 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp<kDppRowMirror>(x);
   return x;
 }
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+// x of the lane N places back in the same row (row_ror:N), N = 1 .. 15.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(N >= 1 && N <= 15, "row rotation");
+  return dpp<0x120 + N>(x);
+}
+
+// ---- across the four 16-lane rows: the row-swap instructions of gfx950 -----------------
+// v_permlane16_swap exchanges rows 1 and 3 of one operand with rows 0 and 2 of the other,
+// v_permlane32_swap the upper half of one with the lower half of the other. With both
+// operands = x, the two results of the first hold (per lane) x and the value 16 lanes away,
+// those of the second x and the value 32 lanes away: VALU operations, no LDS round trip.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const u32x2_t a = __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                false));
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const u32x2_t b = __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                false));
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float x) {
+  const u32x2_t a = __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                false));
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const u32x2_t b = __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                false));
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// Over all 64 lanes; every lane gets the result.
+__device__ __forceinline__ float wave_sum_f32(float x) { return rows4_sum(row16_sum(x)); }
+__device__ __forceinline__ float wave_max_f32(float x) { return rows4_max(row16_max(x)); }
 
 // ---- LDS DMA (global -> LDS without VGPRs) ---------------------------------------------
 // Every lane copies 16 bytes from its own global address; lane i's bytes land at
