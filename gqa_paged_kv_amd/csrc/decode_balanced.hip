@@ -433,16 +433,21 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   uint32_t kb[NB][WS::KROWS][WS::KWORDS], vb[NB][4][W32];
   // append: the row of the step's own token (slot (L - 1) % P of the sequence's last page)
   // is read from k_new / v_new instead of the pool (the pool gets it in consume()).
-  auto load_page = [&](int buf, int cb, int ckv, int cpg) {
-    const size_t page_off = (size_t)page_table[(size_t)cb * max_pages + cpg] * page_stride +
-                            (size_t)ckv * S::PAGE;
+  // live = false: a filler load past the share's end (its data is never used), from the
+  // first block of the pool, which every such load shares (an L2 hit; re-reading the last
+  // page instead would go back to HBM, since the streaming hint does not keep it in L2).
+  auto load_page = [&](int buf, int cb, int ckv, int cpg, bool live) {
+    const size_t page_off =
+        live ? (size_t)page_table[(size_t)cb * max_pages + cpg] * page_stride +
+                   (size_t)ckv * S::PAGE
+             : 0;
     const char* kpage = (const char*)k_cache + page_off;
     const char* kp = kpage + r * S::ROW;
     const char* vp = (const char*)v_cache + page_off + r * S::ROW;
     int new_row = -1;
     if constexpr (APPEND) {
       const int L = seq_len(context_lens, cb, max_pages, 1);
-      if (cpg == (L - 1) / kPage) new_row = (L - 1) % kPage;
+      if (live && cpg == (L - 1) / kPage) new_row = (L - 1) % kPage;
     }
     const size_t new_off = ((size_t)cb * Hkv + ckv) * S::ROW;
     if constexpr (kMq) {
@@ -565,9 +570,9 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   };
 
   // The load cursor runs NB - 1 items ahead of the compute cursor (NB page buffers). The
-  // prefetch is issued on every step (past the share's end it re-reads the current page,
-  // an L2 hit) so that the loads in flight are the same on every path and the wait before
-  // each page is exactly "all but the NB - 2 newest pages".
+  // prefetch is issued on every step (past the share's end as a filler load, see load_page)
+  // so that the loads in flight are the same on every path and the wait before each page
+  // is exactly "all but the NB - 2 newest pages".
   int lb = b, lkv = kvh, lpg = pg, lnp = np;
   auto advance_load = [&]() {
     advance(lb, lkv, lpg, lnp);
@@ -578,17 +583,19 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
       }
     }
   };
-  load_page(0, lb, lkv, lpg);
+  load_page(0, lb, lkv, lpg, true);
 #pragma unroll
   for (int k = 1; k < NB - 1; ++k) {
-    if (lo + k < hi) advance_load();
-    load_page(k, lb, lkv, lpg);
+    const bool live = lo + k < hi;
+    if (live) advance_load();
+    load_page(k, lb, lkv, lpg, live);
   }
   for (long i = lo; i < hi; i += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      if (i + k + NB - 1 < hi) advance_load();
-      load_page((k + NB - 1) % NB, lb, lkv, lpg);
+      const bool live = i + k + NB - 1 < hi;
+      if (live) advance_load();
+      load_page((k + NB - 1) % NB, lb, lkv, lpg, live);
       consume(k, i + k);
       if (i + k + 1 >= hi) break;
     }
