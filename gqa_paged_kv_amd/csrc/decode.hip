@@ -102,7 +102,8 @@ __device__ __forceinline__ void merge_and_store(const WaveState<T, D, DecodeShap
 constexpr int kRegsWaves = 8;
 constexpr int kRegsThreads = kRegsWaves * kWave;
 
-template <typename T, int D, int G>
+// NT: K/V rows read with the streaming hint (see launch_decode for when).
+template <typename T, int D, int G, bool NT>
 __global__ __launch_bounds__(kRegsThreads) void decode_regs_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ context_lens,
@@ -142,8 +143,13 @@ __global__ __launch_bounds__(kRegsThreads) void decode_regs_kernel(
     const size_t off = (size_t)pt_row[lp] * page_stride;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      load_row_nt<T, D>(k_base + off + i * 4 * S::ROW, qd, kb[buf][i]);
-      load_row_nt<T, D>(v_base + off + i * 4 * S::ROW, qd, vb[buf][i]);
+      if constexpr (NT) {
+        load_row_nt<T, D>(k_base + off + i * 4 * S::ROW, qd, kb[buf][i]);
+        load_row_nt<T, D>(v_base + off + i * 4 * S::ROW, qd, vb[buf][i]);
+      } else {
+        load_row<T, D>(k_base + off + i * 4 * S::ROW, qd, kb[buf][i]);
+        load_row<T, D>(v_base + off + i * 4 * S::ROW, qd, vb[buf][i]);
+      }
     }
   };
   auto run = [&](int buf, int lp) {
@@ -653,11 +659,21 @@ static int launch_decode(const void* q, const void* k, const void* v, const int3
     // One KV head per workgroup: its 8 waves take the split's pages round-robin. (Grouping
     // several KV heads per workgroup so that neighbouring (page, kv head) blocks are read
     // together measured no faster, and leaves small batches with too few workgroups.)
+    // The streaming hint on the K/V loads: faster for G >= 2 at every split count measured
+    // (long contexts by 10%), and for G = 1 without splits, but much slower for G = 1 with
+    // splits (B = 256, Hkv = 32, T = 1024, 8 splits: 1225 vs 760 us), where every wave streams
+    // only a few pages of one head.
     const int kvw = 1;
     const int groups = Hkv;
-    hipLaunchKernelGGL((decode_regs_kernel<T, D, G>), dim3(groups * ns, B), dim3(kRegsThreads), 0,
-                       stream, (const T*)q, (const T*)k, (const T*)v, pt, lens, (T*)out, wo, wl,
-                       Hq, Hkv, max_pages, ns, kvw, scale * kLog2e);
+    if (G >= 2 || ns == 1) {
+      hipLaunchKernelGGL((decode_regs_kernel<T, D, G, true>), dim3(groups * ns, B),
+                         dim3(kRegsThreads), 0, stream, (const T*)q, (const T*)k, (const T*)v, pt,
+                         lens, (T*)out, wo, wl, Hq, Hkv, max_pages, ns, kvw, scale * kLog2e);
+    } else {
+      hipLaunchKernelGGL((decode_regs_kernel<T, D, G, false>), dim3(groups * ns, B),
+                         dim3(kRegsThreads), 0, stream, (const T*)q, (const T*)k, (const T*)v, pt,
+                         lens, (T*)out, wo, wl, Hq, Hkv, max_pages, ns, kvw, scale * kLog2e);
+    }
   } else if constexpr (sizeof(T) == 2) {
     // bf16, G >= 16: heads as matrix-core columns
     hipLaunchKernelGGL((decode_mq_kernel<D, G>), dim3(Hkv * ns, B), dim3(kDecodeThreads), 0,
