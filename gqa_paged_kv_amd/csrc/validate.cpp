@@ -109,13 +109,19 @@ extern "C" {
 // (at most 1,024 (sequence, KV head, page) items, or 65,536 with one query head per KV head),
 // which run faster on the split path with at least 16 pages per split (measured with
 // T = 1024, Hq = 32 and B from 1 to 256) provided its partials fit in the workspace past the
-// counters. G >= 16: the split path with auto_splits splits.
+// counters. G >= 16: the split path with auto_splits splits, at least 8 pages per split (with
+// T = 1024 and B = 1 or 16, 8 splits were 9-10% faster than 16, whose 4 pages per split give
+// each of the 4 waves a single page).
 int gqa_decode_balanced_route(int B, int Hq, int Hkv, int D, int max_pages,
                               size_t workspace_bytes) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_pages <= 0 || Hq % Hkv != 0) return -1;
   const int G = Hq / Hkv;
   int ns = auto_splits(B, Hkv);
-  if (G <= 8) {
+  if (G > 8) {
+    const int cap = max_pages / 8 < 1 ? 1 : max_pages / 8;
+    return ns < cap ? ns : cap;
+  }
+  {
     const long items = (long)B * Hkv * max_pages;
     const bool small = items <= (G == 1 ? 65536 : 1024);
     ns = max_pages / 16 < ns ? max_pages / 16 : ns;

@@ -86,7 +86,8 @@ int main() {
   EXPECT(gqa_decode_balanced_route(1, 32, 8, 128, 129, 1 << 30) == 0);
   EXPECT(gqa_decode_balanced_route(1, 1, 1, 128, 65537, 1 << 30) == 0);
   EXPECT(gqa_decode_balanced_route(65535, 32, 32, 128, 1 << 16, 1 << 30) == 0);
-  EXPECT(gqa_decode_balanced_route(1, 32, 1, 128, 64, 1 << 30) == 16);
+  EXPECT(gqa_decode_balanced_route(1, 32, 1, 128, 64, 1 << 30) == 8);     // >= 8 pages per split
+  EXPECT(gqa_decode_balanced_route(1, 32, 1, 128, 4096, 1 << 30) == 16);
   EXPECT(gqa_decode_balanced_route(0, 32, 8, 128, 64, 1 << 30) == -1);
 
   // page-id check over host arrays

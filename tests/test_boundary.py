@@ -96,10 +96,13 @@ def test_balanced_route_limits(lib):
     assert r(2, 8, 2, 128, 16) == 1 and r(2, 8, 2, 128, 31) == 1 and r(2, 8, 2, 128, 32) == 2
     # a workspace that holds only the counters keeps small problems on the persistent kernel
     assert r(2, 32, 8, 128, 64, g.BALANCED_WS_RESERVED) == 0
-    # G >= 16: always the split path, one workgroup per CU (at most 16 splits)
+    # G >= 16: always the split path, one workgroup per CU (at most 16 splits) and at least 8
+    # pages per split
     for B, hkv, ns in ((1, 1, 16), (8, 1, 16), (32, 1, 8), (64, 1, 4), (256, 1, 1), (64, 2, 2)):
-        assert r(B, 32, hkv, 128, 64) == ns, (B, hkv)
         assert r(B, 32, hkv, 128, 100000) == ns, (B, hkv)
+        assert r(B, 32, hkv, 128, 64) == min(ns, 64 // 8), (B, hkv)
+        assert r(B, 32, hkv, 128, 16) == min(ns, 2), (B, hkv)
+    assert r(1, 32, 1, 128, 7) == 1 and r(1, 32, 1, 128, 8) == 1 and r(1, 32, 1, 128, 24) == 3
     assert r(0, 32, 8, 128, 64) == -1 and r(2, 30, 8, 128, 64) == -1
 
 
