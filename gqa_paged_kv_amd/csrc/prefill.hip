@@ -557,32 +557,35 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // V(T-2) in the other stage or, for tile 0, K(0)'s buffer; nothing is loaded over them
   // before the next item starts), and the page ids were fetched into LDS: the append is LDS
   // reads and global stores only.
+  // q0 is a multiple of 16 (BMPOS >= 32), so thread tid of group A always copies 16-byte chunk
+  // c = tid % 16 of page slot tid / 16: row block j (rows 16 j .. 16 j + 15 of the item) is
+  // page-table entry (q0 / 16) + j, tile (q0 + 16 j) / 64, and the row's swizzle depends on the
+  // slot alone. All LDS reads are issued before the first store.
   auto append_from_lds = [&]() {
+    constexpr int NJ = BMPOS / 16;  // row blocks of an item
     const int tid = fresh_lane() + kWave * w;  // group A: 256 threads
+    const int slot = tid >> 4, c = tid & 15;
     const int nrows = min(BMPOS, S - q0);
-    const int total = nrows * 32;  // 16-byte chunks: K then V, 16 per row
-    for (int base = 0; base < total; base += 8 * 4 * kWave) {
-      u32x4_t x[8];
-      bf16_t* dst[8];
+    const uint32_t kx = (uint32_t)((c ^ k_swz(slot)) << 4), vx = (uint32_t)((c ^ v_swz(slot)) << 4);
+    u32x4_t xk[NJ], xv[NJ];
+    int page[NJ];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = min(base + u * 4 * kWave + tid, total - 1);
-        const int is_v = idx >= nrows * 16;
-        const int rem = idx - is_v * nrows * 16;
-        const int pos = q0 + (rem >> 4), c = rem & 15;
-        const int t = pos / BN, row = pos % BN;
-        const uint32_t tile = is_v ? (uint32_t)(t & 1) * 2 * TILE + TILE
-                                   : (t == 0 ? K0_OFF : (uint32_t)(t & 1) * 2 * TILE);
-        const int swz = is_v ? v_swz(row) : k_swz(row);
-        x[u] = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
-            smem0 + tile + row * ROWB + ((c ^ swz) << 4));
-        const int page = *(const __attribute__((address_space(3))) int*)(uintptr_t)(
-            smem0 + PT_OFF + w * 256 + ((pos >> 4) - (q0 >> 4)) * 4);
-        dst[u] = (is_v ? v_cache : k_cache) + (((size_t)page * Hkv + kvh) * 16 + (pos & 15)) * D + c * 8;
+    for (int j = 0; j < NJ; ++j) {
+      const int t = (q0 + 16 * j) / BN;
+      const uint32_t row = (uint32_t)((q0 + 16 * j) % BN + slot) * ROWB;
+      const uint32_t ktile = t == 0 ? K0_OFF : (uint32_t)(t & 1) * 2 * TILE;
+      const uint32_t vtile = (uint32_t)(t & 1) * 2 * TILE + TILE;
+      xk[j] = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(smem0 + ktile + row + kx);
+      xv[j] = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(smem0 + vtile + row + vx);
+      page[j] = *(const __attribute__((address_space(3))) int*)(uintptr_t)(smem0 + PT_OFF + w * 256 + j * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (16 * j + slot < nrows) {
+        const size_t off = (((size_t)page[j] * Hkv + kvh) * 16 + slot) * D + c * 8;
+        *(u32x4_t*)(k_cache + off) = xk[j];
+        *(u32x4_t*)(v_cache + off) = xv[j];
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (base + u * 4 * kWave + tid < total) *(u32x4_t*)dst[u] = x[u];
     }
   };
 
@@ -605,10 +608,19 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   // chunks XOR-swizzled by row % 16) and read back as whole rows, 16 lanes per 256-byte row:
   // each global store then writes four complete rows instead of 16 bytes of each of 32 rows.
   // With qa_e < 0 the tile is only staged (stored later with store_rows).
+  // (l_tot: this lane's partial row sum plus that of the lane 32 away, which holds the row's
+  // other keys; a VALU exchange, so that the LDS traffic of the other wave group's MFMA phase
+  // does not delay it)
+  auto row_total = [&]() {
+    const u32x2_t r = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(l_half), __float_as_uint(l_half),
+                                                  false, false));
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
   auto store_output = [&](uint32_t sbase, int qa_e) {
     const int ln = fresh_lane();
     const int rw = ln & 31, hf = ln >> 5;
-    const float l_tot = l_half + __shfl_xor(l_half, 32);
+    const float l_tot = row_total();
     const float inv = 1.0f / l_tot;  // not finite on rows that are not stored
 #pragma unroll
     for (int mbd = 0; mbd < 4; ++mbd)
@@ -619,17 +631,32 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
         *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)(
             sbase + rw * ROWB + (((4 * mbd + jq) ^ (rw & 15)) << 4) + 8 * hf) = pk;
       }
-    if (qa_e >= 0) {
+    if (qa_e >= 0) {  // all eight rows read back before the first store
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+          out + ((size_t)b * S * Hq + h) * D, 0, (int)((uint32_t)(S - 1) * q_stride + ROWB), 0x00020000);
+      const int c = ln & 15;
+      u32x4_t x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) store_rows(sbase, qa_e, i);
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (ln >> 4);
+        x[i] = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(
+            sbase + rr * ROWB + ((c ^ (rr & 15)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = qa_e + 4 * i + (ln >> 4);
+        const uint32_t off = row < n ? (uint32_t)row * q_stride + c * 16 : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(x[i], ors, (int)off, 0, 0);
+      }
     }
   };
   // Direct form (each lane stores its 4-dim pieces), for group A with G = 2, whose free LDS
-  // stage still holds rows the KV append reads.
+  // stage still holds rows the KV append reads. (For the other group sizes the staged form
+  // measured faster: eight whole-row stores per lane instead of sixteen 8-byte pieces.)
   auto store_output_direct = [&](int qa_e) {
     const int ln = fresh_lane();
     const int my_q = qa_e + (ln & 31);
-    const float l_tot = l_half + __shfl_xor(l_half, 32);
+    const float l_tot = row_total();
     if (my_q < n) {
       const float inv = 1.0f / l_tot;
       bf16_t* orow = out + (((size_t)b * S + my_q) * Hq + h) * D;
