@@ -352,7 +352,7 @@ struct NoQStage {
 // T: q / out element type; TKV: cache element type (T, or an 8-bit float whose per-tensor
 // scales are folded in: k_scale into scale_log2, v_scale into out_scale).
 template <typename T, int D, int G, typename TKV = T, bool APPEND = false>
-__global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
+__global__ __launch_bounds__(kDecodeThreads, (is_fp8<TKV>() && G <= 4) ? 2 : 1) void balanced_kernel(
     const T* __restrict__ q, const TKV* __restrict__ k_cache, const TKV* __restrict__ v_cache,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ context_lens,
     T* __restrict__ out, float* __restrict__ slots, unsigned long long* __restrict__ counters,
@@ -426,6 +426,10 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   constexpr bool kMq = sizeof(T) == 2 && !GQA_DECODE_VALU_SCORES;
   using WS = std::conditional_t<kMq, WaveStateMq<T, D, G, TKV>, WaveState<T, D, G, TKV>>;
   const int qsel = kMq ? lane : qd;  // what init() takes
+  // 8-bit caches: LDS in which merge_rows rearranges the matrix-core PV (one area per wave)
+  constexpr int kStage = (kMq && is_fp8<TKV>()) ? G * D : 4;
+  __shared__ __attribute__((aligned(16))) float pv_stage[kDecodeWaves * kStage];
+  float* const pv_stage_w = pv_stage + wave_id() * kStage;
   // page buffers in VGPRs: NB - 1 pages in flight while one is computed (16-bit caches:
   // 4, which leaves one wave per SIMD with D = 128 and measured faster than two waves with
   // 3; 8-bit caches: 3; fp32 with D = 128 and 8 heads: 2, which fits 512 VGPRs)
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(kDecodeThreads) void balanced_kernel(
   // Finish the segment that ends at item i: merge the 4 DPP rows, then write the output
   // (the whole unit is in this share) or the piece's partial (write-through stores).
   auto finish = [&](long i) {
-    st.merge_rows();
+    if constexpr (kMq) st.merge_rows(pv_stage_w); else st.merge_rows();
     const long first = i - pg;  // first item of the unit (pg = page of item i)
     if (seg_start == first && pg + 1 == np) {
 #pragma unroll

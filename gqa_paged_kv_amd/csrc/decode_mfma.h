@@ -15,7 +15,13 @@
 //   * Q operand: head p*GQ + n % GQ of pass p, the same dims;
 //   * scores: tokens g + 4j (j < 4) of head p*GQ + n % GQ;
 //   * PV: V rows g + 4i (i < 4), dims of lane_dim(n, e), all G heads: the weights of the
-//     other heads come from the lanes of the same quad (DPP quad broadcast).
+//     other heads come from the lanes of the same quad (DPP quad broadcast). 8-bit caches
+//     (whose pages carry half the bytes for the same arithmetic, which the vector PV then
+//     bounds): O^T += V^T P^T on the matrix core instead, one v_mfma_f32_16x16x16_bf16 per
+//     16 dims of a page and score chain, K = the page's 16 tokens in the scores' order
+//     4g + i <-> token g + 4i, so that B = P^T is the lane's own four weights and A = V^T
+//     the lane's own rows (block e: dim lane_dim(n, e)); lane l then holds dims
+//     lane_dim(4g + j, e) of its column's head, rearranged through LDS by merge_rows.
 // The running max is one value per head for the whole wave (raised lazily, as in the
 // vector path, by a wave-wide reduction only when some score exceeds it by 2^8), so the
 // rows of the wave need no rescaling when they are merged.
@@ -24,6 +30,8 @@
 #include "decode_common.h"
 
 namespace gqa {
+
+typedef short s16x4_mq __attribute__((ext_vector_type(4)));  // 4 bf16 operand bits
 
 template <int H>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
@@ -54,11 +62,14 @@ struct WaveStateMq {
   static constexpr int E = D / 16;          // PV dims per lane
   static constexpr int W32 = E / 2;         // bf16 words of a V row per lane
   static constexpr int WKV = kFp8 ? W32 / 2 : W32;
+  static constexpr bool kPvMfma = kFp8;     // PV on the matrix core
+  static constexpr int STAGE_FLOATS = kPvMfma ? G * D : 0;  // LDS per wave for merge_rows
   static_assert(D % 32 == 0 && G % GQ == 0 && NPASS <= 2, "shape");
 
   u32x4_t qb[NPASS][NC];
   float mrun[NPASS], lrun[NPASS];  // this lane's head: reference max, this row's sum
-  float acc[G][E];
+  f32x4_t accm[kPvMfma ? NPASS : 1][kPvMfma ? E : 1];  // matrix-core PV: O^T blocks
+  float acc[G][E];                 // vector PV; matrix-core PV: valid after merge_rows()
   float m[G], l[G];                // per head, valid after merge_rows()
 
   static __device__ __forceinline__ int k_row(int lane) {
@@ -147,15 +158,26 @@ struct WaveStateMq {
       mrun[p] = -INFINITY;
       lrun[p] = 0.f;
     }
+    if constexpr (kPvMfma) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int p = 0; p < NPASS; ++p)
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+        for (int e = 0; e < E; ++e) accm[p][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
   }
 
   // Merge the 4 rows (token groups) of the wave: every lane gets, for all G heads, the
   // group's m, l and the summed acc of its dims. The whole wave must be active.
-  __device__ __forceinline__ void merge_rows() {
+  // stage: this wave's STAGE_FLOATS floats of LDS (matrix-core PV only): the lanes of the
+  // first GQ columns write their head's O^T blocks as [head][e][16 rows], and every lane
+  // reads back dims lane_dim(n, e) = n E + e of every head (row n of block e). One wave
+  // writes and reads its own area, and LDS instructions of a wave complete in order.
+  __device__ __forceinline__ void merge_rows(float* stage = nullptr) {
     float lt[NPASS];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
@@ -165,10 +187,28 @@ struct WaveStateMq {
     for (int h = 0; h < G; ++h) {
       m[h] = quad_bcast(mrun[h / GQ], h % GQ);
       l[h] = quad_bcast(lt[h / GQ], h % GQ);
+    }
+    if constexpr (kPvMfma) {
+      const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      const int n = lane & 15, g = lane >> 4;
+      if (n < GQ) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        acc[h][e] = rows4_sum(acc[h][e]);
+        for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            *(f32x4_t*)(stage + ((p * GQ + n) * E + e) * 16 + 4 * g) = accm[p][e];
       }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = stage[(h * E + e) * 16 + n];
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = rows4_sum(acc[h][e]);
     }
   }
 
@@ -229,11 +269,18 @@ struct WaveStateMq {
         lrun[p] *= alpha[p];
         mrun[p] = m_ref;
       }
+      if constexpr (kPvMfma) {  // the lane's column is one head of each pass
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float a = quad_bcast(alpha[h / GQ], h % GQ);
+        for (int p = 0; p < NPASS; ++p)
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] *= a;
+          for (int e = 0; e < E; ++e) accm[p][e] *= alpha[p];
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float a = quad_bcast(alpha[h / GQ], h % GQ);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[h][e] *= a;
+        }
       }
     }
     // weights of this lane's head, packed as bf16 pairs of tokens (g, g+4), (g+8, g+12)
@@ -269,6 +316,27 @@ struct WaveStateMq {
 #pragma unroll
         for (int y = 0; y < W32; ++y) vb16[i][y] = vw[i][y];
       }
+    }
+    if constexpr (kPvMfma) {
+      // block e = 2y (low halves) and 2y + 1 (high halves): A = (rows 0, 1), (rows 2, 3) of
+      // dim lane_dim(n, e); B = this lane's weights (tokens g, g+4), (g+8, g+12)
+#pragma unroll
+      for (int y = 0; y < W32; ++y) {
+        const uint32_t lo01 = __builtin_amdgcn_perm(vb16[1][y], vb16[0][y], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(vb16[1][y], vb16[0][y], 0x07060302u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(vb16[3][y], vb16[2][y], 0x05040100u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(vb16[3][y], vb16[2][y], 0x07060302u);
+        const s16x4_mq alo = __builtin_bit_cast(s16x4_mq, u32x2_t{lo01, lo23});
+        const s16x4_mq ahi = __builtin_bit_cast(s16x4_mq, u32x2_t{hi01, hi23});
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+          const s16x4_mq bw = __builtin_bit_cast(s16x4_mq, u32x2_t{pk[p][0], pk[p][1]});
+          accm[p][2 * y] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bw, accm[p][2 * y], 0, 0, 0);
+          accm[p][2 * y + 1] =
+              __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bw, accm[p][2 * y + 1], 0, 0, 0);
+        }
+      }
+      return;
     }
     // PV on bf16 pairs (tokens 2j', 2j'+1 of this lane's rows), fp32 accumulation
 #pragma unroll
