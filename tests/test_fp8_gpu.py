@@ -85,3 +85,16 @@ def test_fp8_decode_all_empty_and_clamped(gpu_lib):
                                    c.page_table, torch.tensor([30, 48], dtype=torch.int32),
                                    c.scale, c.fmt)
     assert_close(got, want, "bf16", "fp8 clamped")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_decode_long_context_multilevel_merge(gpu_lib, fmt):
+    """A 32,768-token sequence next to a 100-token one (Hq=32, Hkv=8): each of the long
+    sequence's units spans hundreds of wave shares, so its pieces are merged in groups and
+    then the group partials are merged (the matrix-core PV's blocks pass through the same
+    per-lane layout first). Every output row against the oracle, and a bit-identical rerun."""
+    print(f"[fp8] long context {fmt}", flush=True)
+    x = synth.fp8_decode_inputs(2, 32, 8, 128, 16, [32768, 100], fmt, seed=4096, device=DEV)
+    a = _run(gpu_lib, x)
+    assert_close(a, _ref(x), "bf16", f"fp8 long context {fmt}")
+    assert torch.equal(a, _run(gpu_lib, x))
