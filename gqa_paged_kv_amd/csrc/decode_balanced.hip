@@ -459,12 +459,29 @@ __global__ __launch_bounds__(kDecodeThreads, (is_fp8<TKV>() && G <= 4) ? 2 : 1) 
       WS::load_k(kr == new_row ? (const char*)k_new + new_off : kpage + kr * S::ROW, lane,
                  kb[buf]);
     }
+    if constexpr (kMq && is_fp8<TKV>() && !APPEND) {
+      // 8-bit V rows by 16-byte streaming loads: lanes 2m and 2m + 1 of a row group together
+      // need dims 16m .. 16m + 15 of rows r, r + 4, r + 8, r + 12; the even lane reads rows
+      // r and r + 8, the odd lane rows r + 4 and r + 12 (raw words, rearranged in page()).
+      const char* vpage = (const char*)v_cache + page_off;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = r + 4 * ((qd & 1) + 2 * c);
+        const u32x4_t x = __builtin_nontemporal_load(
+            (const u32x4_t*)(vpage + row * S::ROW + 16 * (qd >> 1)));
+        vb[buf][2 * c][0] = x[0];
+        vb[buf][2 * c][1] = x[1];
+        vb[buf][2 * c + 1][0] = x[2];
+        vb[buf][2 * c + 1][1] = x[3];
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool nr = 4 * i + r == new_row;
       if constexpr (!kMq)
         load_row_nt<TKV, D>(nr ? (const char*)k_new + new_off : kp + i * 4 * S::ROW, qd, kb[buf][i]);
       load_row_nt<TKV, D>(nr ? (const char*)v_new + new_off : vp + i * 4 * S::ROW, qd, vb[buf][i]);
+    }
     }
   };
 

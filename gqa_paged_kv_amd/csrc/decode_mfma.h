@@ -295,6 +295,23 @@ struct WaveStateMq {
       pk[p][0] = pack_bf16x2(w[0], w[1]);
       pk[p][1] = pack_bf16x2(w[2], w[3]);
     }
+    if constexpr (kFp8) {
+      // V arrives as raw 16-byte chunks (see the kernel's load): vw[2c] / vw[2c + 1] hold the
+      // low / high 8 bytes of this lane's chunk c. The lane pair swaps the halves the other
+      // lane needs (DPP quad_perm 1,0,3,2), so that vw[i] becomes row g + 4i, own dims.
+      const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      const bool odd = ln & 1;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int k = 0; k < WKV; ++k) {
+          const uint32_t lo = vw[2 * c][k], hi = vw[2 * c + 1][k];
+          const uint32_t recv =
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? lo : hi), 0xB1, 0xF, 0xF, false);
+          vw[2 * c][k] = odd ? recv : lo;
+          vw[2 * c + 1][k] = odd ? hi : recv;
+        }
+    }
     if constexpr (MASKED) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
