@@ -105,7 +105,7 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t num_reco
 // one pair run on the XCD of its workgroups (workgroup g runs on XCD g % 8, and c % 8 ==
 // g % 8 when 8 divides nbkv) and share its L2. Between two items the workgroup does not
 // drain: the next item's Q rows are fetched into LDS while the current item still runs,
-// and half of an item's output (group B's) is stored after the next item has started.
+// and an item's output is stored (from the Q rows' LDS) after the next item has started.
 template <int G, bool PAGED>
 __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_causal_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -650,33 +650,15 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
       }
     }
   };
-  // Direct form (each lane stores its 4-dim pieces), for group A with G = 2, whose free LDS
-  // stage still holds rows the KV append reads. (For the other group sizes the staged form
-  // measured faster: eight whole-row stores per lane instead of sixteen 8-byte pieces.)
-  auto store_output_direct = [&](int qa_e) {
-    const int ln = fresh_lane();
-    const int my_q = qa_e + (ln & 31);
-    const float l_tot = row_total();
-    if (my_q < n) {
-      const float inv = 1.0f / l_tot;
-      bf16_t* orow = out + (((size_t)b * S + my_q) * Hq + h) * D;
-#pragma unroll
-      for (int mbd = 0; mbd < 4; ++mbd)
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const int dim = 32 * mbd + 8 * jq + 4 * (ln >> 5);
-          const u32x2_t pk = {pack_bf16x2(oacc[mbd][4 * jq + 0] * inv, oacc[mbd][4 * jq + 1] * inv),
-                              pack_bf16x2(oacc[mbd][4 * jq + 2] * inv, oacc[mbd][4 * jq + 3] * inv)};
-          *(u32x2_t*)(orow + dim) = pk;
-        }
-    }
-  };
-  // Group B stages an item's output at the start of the next item (phase 0, in which it has no
-  // other work) in its own Q rows of LDS once it has read them, and stores it between the
-  // MFMAs of its phase 1; group A stores at the end of the item, in phase 2T+1, staged in stage
-  // T % 2, which no wave reads any more then (the append reads tiles T-1 and, with G = 2, T-2).
+  // Both groups store an item's output during the next item: after reading the next item's Q
+  // rows into registers (phase 0) a wave stages its output in those LDS rows, and stores it row
+  // by row between the score MFMAs of its first phase with MFMAs (group A: phase 0, group B:
+  // phase 1). The end of an item then holds only the KV append (group A) and B's last MFMA phase.
+  // With G = 1 group A stores at the end of the item instead (staged in stage T % 2, which no
+  // wave reads then): keeping its output live into the next item spills registers there.
+  constexpr bool kDeferA = G != 1;
   int qa_prev = 0;
-  bool b_pending = false;
+  bool pending = false;
 
   set_lane_offsets();
   {
@@ -713,9 +695,9 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
         qop[s2] = ok ? (t ^ qsign) : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
-    if (w >= 4 && b_pending) {
+    if (pending && (kDeferA || w >= 4)) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the Q rows are in registers
-      store_output(qbuf, -1);  // staged only: stored between the MFMAs of phase 1
+      store_output(qbuf, -1);  // staged only: stored between the score MFMAs below
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
@@ -723,7 +705,13 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     l_half = 0.f;
     even_phase_dma(0, P0{});
     if (w < 4) {
-      if (wave_tiles > 0) scores(PK0{}, [](int) {});
+      if (wave_tiles > 0) {
+        scores(PK0{}, [&](int i) {
+          if (kDeferA && pending) store_rows(qbuf, qa_prev, i);
+        });
+      } else if (kDeferA && pending) {
+        for (int i = 0; i < 8; ++i) store_rows(qbuf, qa_prev, i);
+      }
       for (int t = 0; t < wg_tiles; t += 2) {
         tile_a(t, P0{});
         if (t + 1 < wg_tiles) tile_a(t + 1, P1{});
@@ -733,9 +721,9 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
       bar();  // phase 1
       if (wave_tiles > 0) {
         scores(PK0{}, [&](int i) {
-          if (b_pending) store_rows(qbuf, qa_prev, i);
+          if (pending) store_rows(qbuf, qa_prev, i);
         });
-      } else if (b_pending) {
+      } else if (pending) {
         for (int i = 0; i < 8; ++i) store_rows(qbuf, qa_prev, i);
       }
       for (int t = 0; t < wg_tiles; t += 2) {
@@ -744,18 +732,12 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
       }
     }
     // The next item's Q rows and this item's page ids have landed (requested three phases
-    // earlier); waiting here, before the stores below, keeps the stores' completion off the
-    // next item's start.
+    // earlier); the output stays in registers until the next item's phase 0 (or the end).
     wait_vmcnt<0>();
-    if (w < 4) {
-      if constexpr (G == 2 && !PAGED)
-        store_output_direct(qa);
-      else
-        store_output(smem0 + (uint32_t)(wg_tiles & 1) * 2 * TILE + w * 32 * ROWB, qa);
-    } else {
-      qa_prev = qa;
-      b_pending = true;
-    }
+    if (!kDeferA && w < 4)
+      store_output(smem0 + (uint32_t)(wg_tiles & 1) * 2 * TILE + w * 32 * ROWB, qa);
+    qa_prev = qa;
+    pending = true;
     if constexpr (!PAGED) {
       if (w < 4) {
         if constexpr (G == 1)
@@ -767,7 +749,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     if (!has_next) break;
     r = rn;
   }
-  if (w >= 4) store_output(qbuf, qa);  // no next item: the Q rows are free
+  if (kDeferA || w >= 4) store_output(qbuf, qa);  // no next item: the Q rows are free
   wait_vmcnt<0>();
 }
 
