@@ -10,9 +10,14 @@
 // "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
 // "核心参数调优：PackGQA与NumSplits的协同舞蹈") merged with the log-sum-exp rule.
 //
-// One launch on the caller's stream. Items are ordered b-major, then kv head, then page;
-// N items in all, wave w of nw owns [N w / nw, N (w+1) / nw) (nw: the resident waves, fewer
-// for small batches so that a share holds at least kMinShare items). Every wave computes N
+// One launch on the caller's stream. N items in all, share s of nw is [N s / nw, N (s+1) / nw)
+// (nw: the resident waves, fewer for small batches so that a share holds at least kMinShare
+// items). 16- and 32-bit caches: items are ordered kv-head-major, then b, then page, nw is a
+// multiple of Hkv and wave gw takes share (gw % Hkv) * (nw / Hkv) + gw / Hkv, so share s of
+// kv head s / (nw / Hkv) covers the same (b, page) range for every kv head and the waves of a
+// workgroup read the same pages of consecutive kv heads, whose blocks lie next to each other
+// in the pool, at about the same time. 8-bit caches (two workgroups per compute unit): items
+// ordered b-major, then kv head, then page, and wave gw takes share gw. Every wave computes N
 // and finds the sequence holding its first item with wave-wide scans of ceil(T_b / P). A
 // unit wholly inside one share is finished and written directly; a cut unit leaves, per
 // piece, a partial (normalised output + natural-log LSE) in the share's slot 0 (its first
@@ -388,26 +393,55 @@ __global__ __launch_bounds__(kDecodeThreads, (is_fp8<TKV>() && G <= 4) ? 2 : 1) 
     }
   }
   if (N == 0) return;
-  const int nw = active_waves(N, gridDim.x * kDecodeWaves);
+  // 16- and 32-bit caches: kv-head-major items (measured faster there; slower for the 8-bit
+  // pool, whose kernel runs two workgroups per compute unit)
+  constexpr bool kKvMajor = sizeof(TKV) >= 2;
+  int nw = active_waves(N, gridDim.x * kDecodeWaves);
+  if (kKvMajor && nw >= Hkv) nw -= nw % Hkv;
   if (gw >= nw) return;  // no share: items [N gw / nw, ...) would lie past the last item
-  const long lo = share_lo(N, gw, nw);
-  const long hi = share_lo(N, gw + 1, nw);
+  const int sw = kKvMajor && nw >= Hkv ? (gw % Hkv) * (nw / Hkv) + gw / Hkv : gw;  // the share
+  const long lo = share_lo(N, sw, nw);
+  const long hi = share_lo(N, sw + 1, nw);
   if (lo >= hi) return;
 
-  // ---- locate the sequence holding item lo ----
-  int b = 0, np = 1;
-  long seq_base = 0;  // first item of sequence b
-  locate_item(context_lens, B, Hkv, max_pages, append, lo, lane, n_first, b, np, seq_base);
-  const long rem = lo - seq_base;
-  int kvh = (int)(rem / np);
-  int pg = (int)(rem % np);
+  // ---- locate the kv head and the sequence holding item lo ----
+  int b = 0, np = 1, kvh = 0, pg = 0;
+  if constexpr (kKvMajor) {
+    const long N1 = N / Hkv;  // items of one kv head
+    kvh = (int)(lo / N1);
+    const long lo1 = lo - (long)kvh * N1;
+    long seq_base = 0;  // first item of sequence b within the kv head's items
+    locate_item(context_lens, B, 1, max_pages, append, lo1, lane, n_first, b, np, seq_base);
+    pg = (int)(lo1 - seq_base);
+  } else {
+    long seq_base = 0;  // first item of sequence b
+    locate_item(context_lens, B, Hkv, max_pages, append, lo, lane, n_first, b, np, seq_base);
+    const long rem = lo - seq_base;
+    kvh = (int)(rem / np);
+    pg = (int)(rem % np);
+  }
   const size_t page_stride = (size_t)Hkv * S::PAGE;
 
-  // move a cursor to the next item (skipping empty sequences)
+  // move a cursor to the next item (skipping empty sequences); kv-head-major: the next page,
+  // else the next non-empty sequence, else the first non-empty sequence of the next kv head
+  // (past the last item the cursor holds kv head Hkv, which is never read)
   auto advance = [&](int& cb, int& ckv, int& cpg, int& cnp) {
     if (++cpg == cnp) {
       cpg = 0;
-      if (++ckv == Hkv) {
+      if constexpr (kKvMajor) {
+        int n = 0;
+        do {
+          if (++cb == B) {
+            cb = 0;
+            if (++ckv == Hkv) {
+              n = 1;
+              break;
+            }
+          }
+          n = pages_of(context_lens, cb, max_pages, append);
+        } while (n == 0);
+        cnp = n;
+      } else if (++ckv == Hkv) {
         ckv = 0;
         int n = 0;
         do {
@@ -542,7 +576,7 @@ __global__ __launch_bounds__(kDecodeThreads, (is_fp8<TKV>() && G <= 4) ? 2 : 1) 
       inv[hw] = out_scale / st.l[hw];
       lse[hw] = (st.m[hw] + __builtin_log2f(st.l[hw])) * kLn2;
     }
-    store_piece<D, G>(rs, slot_off(gw, slot), st, inv, lse, lane);
+    store_piece<D, G>(rs, slot_off(sw, slot), st, inv, lse, lane);
     const Piece pc{uniform(first), uniform(np), 1,
                    (size_t)uniform((long)(((size_t)b * Hq + kvh * G) * D))};
     if (slot == 0) piece0 = pc; else piece1 = pc;
@@ -660,7 +694,7 @@ __global__ __launch_bounds__(kDecodeThreads, (is_fp8<TKV>() && G <= 4) ? 2 : 1) 
     const int w1 = share_owner(N, pc.first + pc.np - 1, nw);
     const int npc = w1 - pl.w0 + 1;                                   // pieces of the unit
     pl.s0 = share_lo(N, pl.w0, nw) == pc.first ? 0 : 1;               // slot of piece 0
-    pl.g = (gw - pl.w0) / kGroup;
+    pl.g = (sw - pl.w0) / kGroup;
     pl.gfirst = pl.w0 + pl.g * kGroup;
     pl.gsize = min(kGroup, npc - pl.g * kGroup);
     pl.ngroups = (npc + kGroup - 1) / kGroup;
