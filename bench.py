@@ -227,7 +227,9 @@ def measured_traffic(key):
             h.update(open(os.path.join(CSRC, f), "rb").read())
     except (OSError, KeyError, ValueError):
         return None
-    if h.hexdigest()[:16] != rec["source_sha"]:
+    # equivalent_source_sha: later sources whose build of the counted kernel is the same
+    # device assembly (each with the reason), so the counters still describe it
+    if h.hexdigest()[:16] not in [rec["source_sha"], *rec.get("equivalent_source_sha", {})]:
         return None
     return round(rec["hbm_bytes_per_call"])
 

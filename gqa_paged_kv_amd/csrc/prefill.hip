@@ -47,6 +47,7 @@ constexpr int THREADS = WAVES * kWave;
 constexpr int ROWB = D * 2;     // bytes per K/V row
 constexpr int TILE = BN * ROWB; // 16 KiB
 constexpr float kLazy = 8.0f;   // log2 growth tolerated before rescaling O
+constexpr int kNt = 2;          // cache-policy bit of the buffer builtins: streaming (nt)
 
 // Row swizzles (16-byte chunk index XOR): K rows are read 16 at a time at one chunk,
 // V rows 4 at a time over 4 chunks (transpose reads).
@@ -60,6 +61,18 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 // the issuing wave, then a workgroup barrier) before any wave reads that stage.
 __device__ __forceinline__ void buffer_dma16(u32x4_t rsrc, uint32_t voffset, uint32_t lds) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
+// The same with the streaming (nt) hint, for data read once (the Q rows): it leaves the L2 to
+// the K/V tiles that the other q-tiles of the pair read again. Used for G <= 2, with the
+// output and KV-append stores streamed too: there it measured faster (G = 1: 182 -> 175 us at
+// B=4, S=2048, Hq=32). For G = 4 it cut workload 3's HBM traffic from 1.30x to 1.10x of the
+// algorithmic bytes but took 2-3% longer, so G >= 4 keeps ordinary loads and stores.
+__device__ __forceinline__ void buffer_dma16_nt(u32x4_t rsrc, uint32_t voffset, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                :
                : "v"(voffset), "s"(rsrc), "{m0}"(lds)
                : "memory");
@@ -116,6 +129,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
   using namespace prefill;
   constexpr int BMPOS = 256 / G;  // positions per q-tile
   constexpr int PB = 8 / G;       // 32-position blocks per head
+  constexpr bool kStream = G <= 2;  // streaming hint on Q rows, output and KV-append stores
 
   // LDS: [stage][K, V] tiles (64 KiB); K tile 0, loaded once (16 KiB: every item of the
   // workgroup has the same (b, kv head), hence the same first key tile); the Q rows of
@@ -274,8 +288,12 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     for (int j = 0; j < 8; ++j) {
       const int ri = 4 * j + (ln >> 4);
       const int row = min(qa_item + ri, S - 1);
-      buffer_dma16(rsrc, (uint32_t)row * q_stride + (((ln & 15) ^ (ri & 15)) << 4),
-                   lds + j * 1024);
+      if constexpr (kStream)
+        buffer_dma16_nt(rsrc, (uint32_t)row * q_stride + (((ln & 15) ^ (ri & 15)) << 4),
+                        lds + j * 1024);
+      else
+        buffer_dma16(rsrc, (uint32_t)row * q_stride + (((ln & 15) ^ (ri & 15)) << 4),
+                     lds + j * 1024);
     }
   };
 
@@ -583,8 +601,13 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
     for (int j = 0; j < NJ; ++j) {
       if (16 * j + slot < nrows) {
         const size_t off = (((size_t)page[j] * Hkv + kvh) * 16 + slot) * D + c * 8;
-        *(u32x4_t*)(k_cache + off) = xk[j];
-        *(u32x4_t*)(v_cache + off) = xv[j];
+        if constexpr (kStream) {
+          __builtin_nontemporal_store(xk[j], (u32x4_t*)(k_cache + off));
+          __builtin_nontemporal_store(xv[j], (u32x4_t*)(v_cache + off));
+        } else {
+          *(u32x4_t*)(k_cache + off) = xk[j];
+          *(u32x4_t*)(v_cache + off) = xv[j];
+        }
       }
     }
   };
@@ -601,7 +624,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
         sbase + rr * ROWB + ((c ^ (rr & 15)) << 4));
     const int row = qa_e + rr;
     const uint32_t off = row < n ? (uint32_t)row * q_stride + c * 16 : 0x80000000u;
-    __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)off, 0, kStream ? kNt : 0);
   };
   // Output of one wave's 32 rows (O = O^T / l, bf16). The MFMA layout gives a lane 4
   // consecutive dims of one row, so the tile is first written to 8 KiB of LDS at sbase (16-byte
@@ -646,7 +669,7 @@ __global__ __launch_bounds__(prefill::THREADS) __attribute__((amdgpu_waves_per_e
       for (int i = 0; i < 8; ++i) {
         const int row = qa_e + 4 * i + (ln >> 4);
         const uint32_t off = row < n ? (uint32_t)row * q_stride + c * 16 : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b128(x[i], ors, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(x[i], ors, (int)off, 0, kStream ? kNt : 0);
       }
     }
   };
