@@ -69,8 +69,9 @@ __device__ __forceinline__ void buffer_dma16(u32x4_t rsrc, uint32_t voffset, uin
 // The same with the streaming (nt) hint, for data read once (the Q rows): it leaves the L2 to
 // the K/V tiles that the other q-tiles of the pair read again. Used for G <= 2, with the
 // output and KV-append stores streamed too: there it measured faster (G = 1: 182 -> 175 us at
-// B=4, S=2048, Hq=32). For G = 4 it cut workload 3's HBM traffic from 1.30x to 1.10x of the
-// algorithmic bytes but took 2-3% longer, so G >= 4 keeps ordinary loads and stores.
+// B=4, S=2048, Hq=32). For G = 4 (B=4, S=2048, Hq=32, Hkv=8) it cut the HBM traffic from 1.30x
+// to 1.10x of the algorithmic bytes but took 2-3% longer, so G >= 4 keeps ordinary loads and
+// stores.
 __device__ __forceinline__ void buffer_dma16_nt(u32x4_t rsrc, uint32_t voffset, uint32_t lds) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                :
