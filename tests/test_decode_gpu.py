@@ -278,6 +278,39 @@ def test_balanced_config1_and_empty_sequences(gpu_lib, route):
     assert_close(out, _ref(y), "bf16", f"balanced empty {route}")
 
 
+# The persistent kernel walks 16- and 32-bit caches kv-head-major: a share runs through the
+# sequences of one kv head, skipping empty ones, and wraps to the first non-empty sequence of
+# the next kv head; the resident waves are rounded down to a multiple of Hkv. Batches of more
+# than 64 sequences (the start-up scan's chunk), empty sequences at both ends and in runs, and
+# kv-head counts that do not divide the wave count.
+def _walk_lens(B, seed):
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(1, 700, (B,), generator=g)
+    for i in (0, 1, B // 2, B // 2 + 1, B // 2 + 2, B - 2, B - 1):
+        lens[i] = 0
+    return [int(t) for t in lens]
+
+
+WALK_CASES = [
+    ("bf16", 128, 32, 8, 100),
+    ("bf16", 128, 12, 3, 70),
+    ("bf16", 64, 10, 5, 67),
+    ("f32", 128, 16, 4, 66),
+]
+
+
+@pytest.mark.parametrize("case", WALK_CASES, ids=lambda c: f"{c[0]}-D{c[1]}-{c[2]}x{c[3]}-B{c[4]}")
+def test_balanced_kv_head_major_walk(gpu_lib, case):
+    dtype, D, hq, hkv, B = case
+    print(f"[balanced] kv-head-major walk {case}", flush=True)
+    lens = _walk_lens(B, seed=B + hkv)
+    x = _bal_inputs(gpu_lib, "persistent", B, hq, hkv, D, lens, dtype, seed=3 * B + hq)
+    out = _run_bal(gpu_lib, x)
+    assert_close(out, _ref(x), dtype, f"balanced walk {case}")
+    again = _run_bal(gpu_lib, x)
+    assert torch.equal(out, again), "a second call differs"
+
+
 def test_balanced_config2_parity_determinism_permutation(gpu_lib, cfg2):
     print("[balanced] config2", flush=True)
     x, ref = cfg2
