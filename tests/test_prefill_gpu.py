@@ -87,6 +87,23 @@ def test_config3_prefill_whole_output_and_append(gpu_lib, cfg3):
     assert_close(out, ref, "bf16", "config3 whole output")
 
 
+@pytest.mark.parametrize("hkv", [32, 16])
+def test_prefill_full_size_small_groups_whole_output(gpu_lib, hkv):
+    """B=4, S=2048, Hq=32 with G = 1 and G = 2 (the kernels that stream their Q rows, output
+    and append with the nt hint): every head against the oracle, the whole append, and a
+    bit-identical second call."""
+    print(f"[prefill] full size Hkv={hkv}", flush=True)
+    x = synth.prefill_inputs(4, 2048, 32, hkv, 128, 16, seed=4000 + hkv, device=DEV)
+    kb, vb = x.k_cache.cpu(), x.v_cache.cpu()
+    out = _run(gpu_lib, x)
+    _check_append(x, kb, vb)
+    again = _run(gpu_lib, x)
+    assert torch.equal(out, again), "a second call differs"
+    c = x.to("cpu")
+    ref = oracle.prefill_causal(c.q, c.k, c.v, c.scale)
+    assert_close(out, ref, "bf16", f"prefill full size Hkv={hkv}")
+
+
 def test_prefill_long_sequence_whole_output(gpu_lib):
     """S = 8192 (4x the benchmark length: 128 key tiles for the last q-tile, the running max
     raised many times): every head against the oracle, and the append of all 8192 positions."""
