@@ -105,11 +105,14 @@ size_t slot_area_bytes(int G, int D) {
 
 extern "C" {
 
-// Route of the balanced entry point. G <= 8: the persistent kernel, except for small problems
-// (at most 1,024 (sequence, KV head, page) items, or 65,536 with one query head per KV head),
-// which run faster on the split path with at least 16 pages per split (measured with
-// T = 1024, Hq = 32 and B from 1 to 256) provided its partials fit in the workspace past the
-// counters. G >= 16: the split path with auto_splits splits, at least 8 pages per split (with
+// Route of the balanced entry point. G <= 8: the persistent kernel, except for small problems,
+// which run faster on the split path with at least 16 pages per split, provided its partials
+// fit in the workspace past the counters: at most 1,024 (sequence, KV head, page) items (any
+// G <= 8; measured with T = 1024, Hq = 32 and B from 1 to 256), or 65,536 with one query head
+// per KV head, or, for G = 2 and G = 4, at most 16,384 / 8,192 items when the split path takes
+// at most 4 splits of page-table rows of at least 16 pages (uniform and ragged batches,
+// Hq = 32: the split path at 0.64-1.02 of the persistent kernel's time there, and slower with
+// 8 or 16 splits, with 8-page rows, and at G = 8). G >= 16: the split path with auto_splits splits, at least 8 pages per split (with
 // T = 1024 and B = 1 or 16, 8 splits were 9-10% faster than 16, whose 4 pages per split give
 // each of the 4 waves a single page).
 int gqa_decode_balanced_route(int B, int Hq, int Hkv, int D, int max_pages,
@@ -123,9 +126,11 @@ int gqa_decode_balanced_route(int B, int Hq, int Hkv, int D, int max_pages,
   }
   {
     const long items = (long)B * Hkv * max_pages;
-    const bool small = items <= (G == 1 ? 65536 : 1024);
     ns = max_pages / 16 < ns ? max_pages / 16 : ns;
     if (ns < 1) ns = 1;
+    const long mid = G == 2 ? 16384 : (G == 4 ? 8192 : 0);  // few splits, rows of 16+ pages
+    const bool small = items <= (G == 1 ? 65536 : 1024) ||
+                       (items <= mid && ns <= 4 && max_pages >= 16);
     const size_t split_bytes = ns == 1 ? 0 : gqa_decode_workspace_bytes(B, Hq, D, ns);
     if (!small || GQA_BALANCED_WS_RESERVED + split_bytes > workspace_bytes) return 0;
   }

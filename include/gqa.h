@@ -114,8 +114,9 @@ int gqa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  * its pieces with the log-sum-exp merge of gqa_combine_splits (the NumSplits
  * decomposition of page "解锁GQA性能潜力：从批量大小敏感性到高效优化实践", section
  * "核心参数调优：PackGQA与NumSplits的协同舞蹈"). For G >= 16, and for small problems
- * (B * Hkv * max_pages at most 1,024, or 65,536 when G = 1, if the split partials fit in the
- * workspace past its counters) it runs the split path with an automatic split count; see
+ * (B * Hkv * max_pages at most 1,024, or 65,536 when G = 1, or 16,384 / 8,192 when G = 2 / 4
+ * with at most 4 splits of rows of at least 16 pages; in each case if the split partials fit
+ * in the workspace past its counters) it runs the split path with an automatic split count; see
  * gqa_decode_balanced_route. The route depends on the page-table row width max_pages, not
  * on the live lengths: a table sized for a long maximum context always takes the persistent
  * kernel.

@@ -77,21 +77,27 @@ def test_balanced_workspace_layout(lib):
 
 
 def test_balanced_route_limits(lib):
-    """The balanced entry point's route: the persistent kernel (0) above 1,024 (sequence, KV
-    head, page) items (65,536 for G = 1), the split path (n >= 1 splits) at or below, the split
-    path for G >= 16 at every size, and the persistent kernel whenever the split partials
-    would not fit in the workspace."""
+    """The balanced entry point's route: the split path (n >= 1 splits) at or below 1,024
+    (sequence, KV head, page) items (65,536 for G = 1), and for G = 2 / G = 4 at or below
+    16,384 / 8,192 items when it takes at most 4 splits of rows of at least 16 pages; the
+    persistent kernel (0) otherwise; the split path for G >= 16 at every size, and the
+    persistent kernel whenever the split partials would not fit in the workspace."""
     r = g.balanced_route
-    # G = 4: B * Hkv * max_pages = 1024 / 1025
+    # G = 4: B * Hkv * max_pages = 1024 / 1032 with 8 splits
     assert r(2, 32, 8, 128, 64) >= 1 and r(2, 32, 8, 128, 64) == min(256 // 16, 64 // 16)
     assert r(1, 32, 8, 128, 128) >= 1 and r(1, 32, 8, 128, 129) == 0
-    assert r(5, 20, 5, 128, 41) == 0 and r(5, 20, 5, 128, 40) >= 1  # 1025 vs 1000 items
+    assert r(2, 32, 8, 128, 128) == 0  # 2,048 items, 8 splits
+    # G = 4, at most 4 splits of 16+ page rows: 8192 / 8256 items
+    assert r(5, 20, 5, 128, 41) == 2 and r(5, 20, 5, 128, 40) >= 1  # 1025 / 1000 items
+    assert r(8, 32, 8, 128, 128) == 4 and r(8, 32, 8, 128, 129) == 0
+    assert r(64, 32, 8, 128, 8) == 0 and r(64, 32, 8, 128, 16) == 1  # 8-page rows
     # G = 1: 65536 / 65537 items
     assert r(8, 8, 8, 128, 1024) >= 1 and r(8, 8, 8, 128, 1025) == 0
     assert r(1, 1, 1, 128, 65536) >= 1 and r(1, 1, 1, 128, 65537) == 0
-    # G = 8 and G = 2 follow the 1,024 rule
+    # G = 8 follows the 1,024 rule; G = 2 the 16,384 one (16384 / 16512 items)
     assert r(4, 32, 4, 64, 64) >= 1 and r(4, 32, 4, 64, 65) == 0
-    assert r(1, 32, 16, 128, 64) >= 1 and r(1, 32, 16, 128, 65) == 0
+    assert r(1, 32, 16, 128, 64) >= 1 and r(1, 32, 16, 128, 65) == 4
+    assert r(8, 32, 16, 128, 128) == 2 and r(8, 32, 16, 128, 129) == 0
     # narrow tables: at least 16 pages per split, so fewer than 32 pages means one split
     assert r(2, 8, 2, 128, 16) == 1 and r(2, 8, 2, 128, 31) == 1 and r(2, 8, 2, 128, 32) == 2
     # a workspace that holds only the counters keeps small problems on the persistent kernel

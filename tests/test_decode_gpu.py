@@ -230,10 +230,11 @@ def _run_bal(g, x):
 def _route_table(route, B, hq, hkv, lens):
     """Page-table width that sends a balanced call down `route`: "split" keeps the narrowest
     table (small problems take the split path), "persistent" widens it past the small-problem
-    limit (1,024 (sequence, KV head, page) items, 65,536 for G = 1)."""
+    limits ((sequence, KV head, page) items: 65,536 for G = 1, 16,384 for G = 2, 8,192 for
+    G = 4, 1,024 for G = 8)."""
     if route == "split":
         return None
-    limit = 65536 if hq // hkv == 1 else 1024
+    limit = {1: 65536, 2: 16384, 4: 8192}.get(hq // hkv, 1024)
     return max(max((t + 15) // 16 for t in lens), 1, limit // (B * hkv) + 1)
 
 
@@ -382,7 +383,7 @@ def test_balanced_all_sequences_empty_and_clamped_lengths(gpu_lib, route):
         assert torch.all(out == 0), f"all empty {dtype} {hq}x{hkv}"
     # rows 1 and 2 fill their page-table rows (mp pages), row 0 holds 40 tokens; only rows
     # whose table is full get a length past it
-    mp = 4 if route == "split" else 43  # 3 * 8 * 43 = 1032 items > 1024
+    mp = 4 if route == "split" else 342  # 3 * 8 * 342 = 8208 items > 8192: persistent
     full = mp * 16
     x = _bal_inputs(gpu_lib, route, 3, 32, 8, 128, [40, full, full], "bf16", seed=62)
     assert x.page_table.shape[1] == mp
@@ -395,7 +396,9 @@ def test_balanced_all_sequences_empty_and_clamped_lengths(gpu_lib, route):
 
 
 @pytest.mark.parametrize("B,hq,hkv,mp,route", [
-    (4, 32, 8, 32, "split"), (5, 20, 5, 41, "persistent"),        # G = 4: 1,024 / 1,025 items
+    (4, 32, 8, 32, "split"), (1, 32, 8, 129, "persistent"),       # G = 4: 1,024 / 1,032 items
+    (8, 32, 8, 128, "split"), (8, 32, 8, 129, "persistent"),      # G = 4, 4 splits: 8,192 / 8,256
+    (8, 32, 16, 128, "split"), (8, 32, 16, 129, "persistent"),    # G = 2: 16,384 / 16,512
     (2, 8, 8, 4096, "split"), (1, 1, 1, 65537, "persistent"),     # G = 1: 65,536 / 65,537
 ])
 def test_balanced_route_limit_parity(gpu_lib, B, hq, hkv, mp, route):
@@ -404,7 +407,7 @@ def test_balanced_route_limit_parity(gpu_lib, B, hq, hkv, mp, route):
     lens = [(37 * (b + 3)) % (mp * 16) + 1 for b in range(B)]
     x = synth.decode_inputs(B, hq, hkv, 128, 16, lens, "bf16", seed=mp + B, device=DEV,
                             max_pages=mp)
-    assert B * hkv * mp in (1024, 1025, 65536, 65537)
+    assert B * hkv * mp in (1024, 1032, 8192, 8256, 16384, 16512, 65536, 65537)
     assert (gpu_lib.balanced_route(B, hq, hkv, 128, mp) == 0) == (route == "persistent")
     assert_close(_run_bal(gpu_lib, x), _ref(x), "bf16", f"route limit {route}")
 
